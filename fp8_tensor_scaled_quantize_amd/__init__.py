@@ -1,0 +1,168 @@
+"""fp8mi: FP8 per-tensor scaled quantize, delayed-scaling amax history fold
+and per-tensor-scaled fp8 GEMM on MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/fp8mi.h (libfp8mi.so).  The
+functions carry the ABI's names and only marshal arguments: shapes, strides
+and device pointers of torch tensors, and torch's current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; when the library
+is missing, every call raises.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import lib
+
+__all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual",
+           "fp8_amax_fold", "fp8_mm", "new_ring", "ring_words", "version"]
+
+E4M3, E5M2 = 0, 1
+F32, F16, BF16 = 0, 1, 2
+
+_FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"fp8mi status {status}: {detail}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise Fp8Error(status, f"{L.fp8mi_status_string(status).decode()} -- {L.fp8mi_last_error().decode()}")
+
+
+def _fmt(f) -> int:
+    try:
+        return _FMT[f]
+    except KeyError:
+        raise ValueError(f"unknown fp8 format {f!r}") from None
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _as_codes(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype != torch.uint8 else t
+
+
+def _ring_args(ring):
+    if ring is None:
+        return None, 0
+    if ring.dim() != 1 or ring.dtype not in (torch.int32, torch.uint32) or not ring.is_contiguous():
+        raise ValueError("ring must be a contiguous 1-D int32 tensor of hist_len + 4 words")
+    return ring.data_ptr(), ring.numel() - 4
+
+
+def version() -> str:
+    return lib().fp8mi_version().decode()
+
+
+def new_ring(hist_len: int, scale0: float = 1.0, device=None) -> torch.Tensor:
+    """A zeroed ring (history 0, slot 0, ticket 0, accumulator 0) holding
+    scale0 as its current scale: hist_len + 4 int32 words on `device`."""
+    w = torch.zeros(hist_len + 4, dtype=torch.int32)
+    w[hist_len] = torch.tensor([scale0], dtype=torch.float32).view(torch.int32)[0]
+    return w.to(device if device is not None else "cuda")
+
+
+def ring_words(ring: torch.Tensor):
+    """Host copy of a ring: dict of hist (fp32), scale, idx, ticket, acc."""
+    w = ring.detach().to("cpu")
+    h = w.numel() - 4
+    f = w.view(torch.float32)
+    return {"hist": f[:h].clone(), "scale": float(f[h]), "idx": int(w[h + 1]),
+            "ticket": int(w[h + 2]), "acc": int(w[h + 3])}
+
+
+def fp8_quantize(x: torch.Tensor, fmt, transposed: bool = False, out: torch.Tensor | None = None,
+                 scale: torch.Tensor | None = None, ring: torch.Tensor | None = None,
+                 scale_inv_out: torch.Tensor | None = None, amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    """Quantize a 2-D bf16/fp16/fp32 tensor (unit column stride; any row
+    stride and base offset) to fp8 codes (uint8) in row or transposed layout.
+    Exactly one of `scale` (device fp32 scalar) or `ring` is given."""
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    f = _fmt(fmt)
+    if out is None:
+        out = torch.empty((cols, rows) if transposed else (rows, cols), dtype=torch.uint8, device=x.device)
+    out = _as_codes(out)
+    ld_x = x.stride(0) if rows > 1 else cols
+    ld_out = out.stride(0) if out.shape[0] > 1 else out.shape[1]
+    rp, h = _ring_args(ring)
+    _check(lib().fp8_quantize(_ptr(x), _DT[x.dtype], rows, cols, ld_x, f, int(bool(transposed)), _ptr(out),
+                              ld_out, _ptr(scale), rp, h, _ptr(scale_inv_out), _ptr(amax_out), _stream(x)))
+    return out
+
+
+def fp8_quantize_dual(x: torch.Tensor, fmt, out_row: torch.Tensor | None = None, out_t: torch.Tensor | None = None,
+                      scale: torch.Tensor | None = None, ring: torch.Tensor | None = None,
+                      scale_inv_out: torch.Tensor | None = None, amax_out: torch.Tensor | None = None):
+    """Both layouts from one read; returns (codes [rows, cols], codes_t [cols, rows])."""
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    f = _fmt(fmt)
+    if out_row is None:
+        out_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if out_t is None:
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    out_row, out_t = _as_codes(out_row), _as_codes(out_t)
+    ld_x = x.stride(0) if rows > 1 else cols
+    ld_r = out_row.stride(0) if out_row.shape[0] > 1 else out_row.shape[1]
+    ld_t = out_t.stride(0) if out_t.shape[0] > 1 else out_t.shape[1]
+    rp, h = _ring_args(ring)
+    _check(lib().fp8_quantize_dual(_ptr(x), _DT[x.dtype], rows, cols, ld_x, f, _ptr(out_row), ld_r, _ptr(out_t),
+                                   ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out), _ptr(amax_out), _stream(x)))
+    return out_row, out_t
+
+
+def fp8_amax_fold(ring: torch.Tensor, amax: torch.Tensor, fmt) -> None:
+    """Fold a device fp32 amax into the ring (the fold a ring-mode quantize
+    performs in its last workgroup)."""
+    rp, h = _ring_args(ring)
+    _check(lib().fp8_amax_fold(rp, h, _ptr(amax), _fmt(fmt), _stream(ring)))
+
+
+def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_inv: torch.Tensor | None = None,
+           b_scale_inv: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = bf16(A B^T * sa * sb + bias) for fp8 codes A [(batch,) M, K] and
+    B [(batch,) N, K]; a size-1 (or stride-0) batch dimension broadcasts."""
+    a, b = _as_codes(a), _as_codes(b)
+    a3 = a if a.dim() == 3 else a.unsqueeze(0)
+    b3 = b if b.dim() == 3 else b.unsqueeze(0)
+    if a3.shape[-1] != b3.shape[-1]:
+        raise ValueError(f"K mismatch: {tuple(a.shape)} vs {tuple(b.shape)}")
+    batch = max(a3.shape[0], b3.shape[0])
+    if a3.shape[0] not in (1, batch) or b3.shape[0] not in (1, batch):
+        raise ValueError("batch sizes must match or be 1")
+    M, K = a3.shape[1], a3.shape[2]
+    N = b3.shape[1]
+    for t in (a3, b3):
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("operands need unit stride along K")
+    sa = 0 if a3.shape[0] == 1 else a3.stride(0)
+    sb = 0 if b3.shape[0] == 1 else b3.stride(0)
+    lda = a3.stride(1) if M > 1 else K
+    ldb = b3.stride(1) if N > 1 else K
+    if out is None:
+        shape = (batch, M, N) if (a.dim() == 3 or b.dim() == 3) else (M, N)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=a.device)
+    c3 = out if out.dim() == 3 else out.unsqueeze(0)
+    ldc = c3.stride(1) if M > 1 else N
+    sc = c3.stride(0) if batch > 1 else M * ldc
+    bias_dt = _DT[bias.dtype] if bias is not None else 0
+    _check(lib().fp8_mm(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
+                        _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(out), ldc, sc, _stream(a)))
+    return out

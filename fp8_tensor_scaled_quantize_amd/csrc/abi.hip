@@ -1,0 +1,189 @@
+// C ABI of libfp8mi: argument validation, status reporting and dispatch to
+// the kernel launchers.  Every check runs before any HIP call, so a rejected
+// call has no side effects.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fp8mi.h"
+#include "fp8mi_internal.h"
+
+namespace fp8mi {
+
+static thread_local char g_err[512] = "";
+
+static fp8mi_status fail(fp8mi_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+static fp8mi_status from_hip(hipError_t e, const char* where) {
+  if (e == hipSuccess) return FP8MI_OK;
+  return fail(FP8MI_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+static bool valid_fmt(int f) { return f == FP8MI_E4M3 || f == FP8MI_E5M2; }
+static bool valid_dtype(int d) { return d == FP8MI_F32 || d == FP8MI_F16 || d == FP8MI_BF16; }
+static int dtype_bytes(int d) { return d == FP8MI_F32 ? 4 : 2; }
+
+static fp8mi_status check_scale_ring(const float* scale, uint32_t* ring, int32_t H) {
+  if ((scale == nullptr) == (ring == nullptr))
+    return fail(FP8MI_ERR_ARG, "give exactly one of scale and ring (scale=%p ring=%p)", (const void*)scale,
+                (void*)ring);
+  if (ring) {
+    if (H < 1 || H > FP8MI_MAX_HIST) return fail(FP8MI_ERR_SHAPE, "hist_len %d outside [1, %d]", H, FP8MI_MAX_HIST);
+    if (reinterpret_cast<uintptr_t>(ring) & 3u) return fail(FP8MI_ERR_ARG, "ring must be 4-byte aligned");
+  }
+  return FP8MI_OK;
+}
+
+static fp8mi_status check_input(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x) {
+  if (!valid_dtype(dt)) return fail(FP8MI_ERR_ENUM, "x_dtype %d is not FP8MI_F32/F16/BF16", dt);
+  if (rows < 0 || cols < 0) return fail(FP8MI_ERR_SHAPE, "negative shape rows=%lld cols=%lld", (long long)rows,
+                                        (long long)cols);
+  if (rows > 0 && ld_x < cols) return fail(FP8MI_ERR_SHAPE, "ld_x %lld < cols %lld", (long long)ld_x, (long long)cols);
+  if (rows > 0 && cols > 0 && x == nullptr) return fail(FP8MI_ERR_NULL, "x is NULL");
+  if (reinterpret_cast<uintptr_t>(x) % dtype_bytes(dt)) return fail(FP8MI_ERR_ARG, "x not aligned to its element size");
+  return FP8MI_OK;
+}
+
+static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                                    int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
+                                    const float* scale, uint32_t* ring, int32_t H, float* scale_inv_out,
+                                    float* amax_out, void* stream) {
+  fp8mi_status s = check_input(x, dt, rows, cols, ld_x);
+  if (s != FP8MI_OK) return s;
+  if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
+  s = check_scale_ring(scale, ring, H);
+  if (s != FP8MI_OK) return s;
+  const bool any = rows > 0 && cols > 0;
+  if (mode != 1) {
+    if (any && !out_row) return fail(FP8MI_ERR_NULL, "row-layout output is NULL");
+    if (rows > 0 && ld_row < cols) return fail(FP8MI_ERR_SHAPE, "row-layout ld %lld < cols %lld", (long long)ld_row,
+                                               (long long)cols);
+  }
+  if (mode != 0) {
+    if (any && !out_t) return fail(FP8MI_ERR_NULL, "transposed output is NULL");
+    if (cols > 0 && ld_t < rows) return fail(FP8MI_ERR_SHAPE, "transposed ld %lld < rows %lld", (long long)ld_t,
+                                             (long long)rows);
+  }
+  if (reinterpret_cast<uintptr_t>(scale) & 3u || reinterpret_cast<uintptr_t>(scale_inv_out) & 3u ||
+      reinterpret_cast<uintptr_t>(amax_out) & 3u)
+    return fail(FP8MI_ERR_ARG, "fp32 scalars must be 4-byte aligned");
+  hipError_t e = launch_quantize(x, dt, rows, cols, ld_x, fmt, mode, out_row, ld_row, out_t, ld_t, scale, ring, H,
+                                 scale_inv_out, amax_out, static_cast<hipStream_t>(stream));
+  return from_hip(e, "quantize launch");
+}
+
+}  // namespace fp8mi
+
+using namespace fp8mi;
+
+extern "C" {
+
+fp8mi_status fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                          int transposed, uint8_t* out, int64_t ld_out, const float* scale, uint32_t* ring,
+                          int32_t hist_len, float* scale_inv_out, float* amax_out, void* stream) {
+  if (transposed != 0 && transposed != 1) return fail(FP8MI_ERR_ENUM, "transposed must be 0 or 1, got %d", transposed);
+  if (transposed)
+    return quantize_common(x, x_dtype, rows, cols, ld_x, fmt, 1, nullptr, 0, out, ld_out, scale, ring, hist_len,
+                           scale_inv_out, amax_out, stream);
+  return quantize_common(x, x_dtype, rows, cols, ld_x, fmt, 0, out, ld_out, nullptr, 0, scale, ring, hist_len,
+                         scale_inv_out, amax_out, stream);
+}
+
+fp8mi_status fp8_quantize_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                               uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t, const float* scale,
+                               uint32_t* ring, int32_t hist_len, float* scale_inv_out, float* amax_out,
+                               void* stream) {
+  return quantize_common(x, x_dtype, rows, cols, ld_x, fmt, 2, out_row, ld_row, out_t, ld_t, scale, ring, hist_len,
+                         scale_inv_out, amax_out, stream);
+}
+
+fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const float* amax, int fmt, void* stream) {
+  if (!ring) return fail(FP8MI_ERR_NULL, "ring is NULL");
+  if (!amax) return fail(FP8MI_ERR_NULL, "amax is NULL");
+  if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
+  fp8mi_status s = check_scale_ring(nullptr, ring, hist_len);
+  if (s != FP8MI_OK) return s;
+  return from_hip(launch_amax_fold(ring, hist_len, amax, fmt, static_cast<hipStream_t>(stream)), "fold launch");
+}
+
+fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, const uint8_t* b, int fmt_b,
+                    int64_t ldb, int64_t stride_b, int64_t M, int64_t N, int64_t K, int64_t batch,
+                    const float* a_scale_inv, const float* b_scale_inv, const void* bias, int bias_dtype, void* c,
+                    int64_t ldc, int64_t stride_c, void* stream) {
+  if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b))
+    return fail(FP8MI_ERR_ENUM, "fmt_a %d / fmt_b %d must be FP8MI_E4M3/FP8MI_E5M2", fmt_a, fmt_b);
+  if (bias && !valid_dtype(bias_dtype)) return fail(FP8MI_ERR_ENUM, "bias_dtype %d is not F32/F16/BF16", bias_dtype);
+  if (M < 0 || N < 0 || K < 0 || batch < 0)
+    return fail(FP8MI_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld batch=%lld", (long long)M, (long long)N,
+                (long long)K, (long long)batch);
+  if (M == 0 || N == 0 || batch == 0) return FP8MI_OK;
+  if (!c) return fail(FP8MI_ERR_NULL, "c is NULL");
+  if (K > 0 && (!a || !b)) return fail(FP8MI_ERR_NULL, "a or b is NULL");
+  if (ldc < N) return fail(FP8MI_ERR_SHAPE, "ldc %lld < N %lld", (long long)ldc, (long long)N);
+  if (K > 0 && (lda < K || ldb < K))
+    return fail(FP8MI_ERR_SHAPE, "lda %lld / ldb %lld < K %lld", (long long)lda, (long long)ldb, (long long)K);
+  if (stride_a < 0 || stride_b < 0 || stride_c < 0) return fail(FP8MI_ERR_STRIDE, "negative batch stride");
+  if (batch > 1 && stride_c < M * ldc)
+    return fail(FP8MI_ERR_STRIDE, "stride_c %lld < M*ldc %lld: batches would overlap", (long long)stride_c,
+                (long long)(M * ldc));
+  if (reinterpret_cast<uintptr_t>(c) & 1u) return fail(FP8MI_ERR_ARG, "c must be 2-byte aligned");
+  if (bias && (reinterpret_cast<uintptr_t>(bias) % dtype_bytes(bias_dtype)))
+    return fail(FP8MI_ERR_ARG, "bias not aligned to its element size");
+  if (K > 0) {
+    if ((K % 16) || (lda % 16) || (ldb % 16))
+      return fail(FP8MI_ERR_UNSUPPORTED, "K, lda and ldb must be multiples of 16 (K=%lld lda=%lld ldb=%lld)",
+                  (long long)K, (long long)lda, (long long)ldb);
+    if ((reinterpret_cast<uintptr_t>(a) & 15u) || (reinterpret_cast<uintptr_t>(b) & 15u))
+      return fail(FP8MI_ERR_UNSUPPORTED, "a and b must be 16-byte aligned");
+    if ((stride_a % 16) || (stride_b % 16))
+      return fail(FP8MI_ERR_UNSUPPORTED, "batch strides of a and b must be multiples of 16");
+  }
+  if ((M + 63) / 64 > 65535 || batch > 65535)
+    return fail(FP8MI_ERR_UNSUPPORTED, "M=%lld / batch=%lld beyond the launch grid", (long long)M, (long long)batch);
+  MmArgs p{a, b, lda, ldb, stride_a, stride_b, M, N, K, batch, a_scale_inv, b_scale_inv,
+           bias, bias ? bias_dtype : -1, static_cast<uint16_t*>(c), ldc, stride_c};
+  return from_hip(launch_mm(p, fmt_a, fmt_b, static_cast<hipStream_t>(stream)), "mm launch");
+}
+
+const char* fp8mi_status_string(int s) {
+  switch (s) {
+    case FP8MI_OK: return "ok";
+    case FP8MI_ERR_NULL: return "required pointer is NULL";
+    case FP8MI_ERR_ENUM: return "enum value out of range";
+    case FP8MI_ERR_SHAPE: return "invalid shape or leading dimension";
+    case FP8MI_ERR_STRIDE: return "invalid batch stride";
+    case FP8MI_ERR_UNSUPPORTED: return "unsupported layout or alignment";
+    case FP8MI_ERR_HIP: return "HIP runtime error";
+    case FP8MI_ERR_ARG: return "inconsistent arguments";
+    default: return "unknown status";
+  }
+}
+
+const char* fp8mi_last_error(void) { return g_err; }
+
+const char* fp8mi_version(void) { return "fp8mi 0.1 gfx950"; }
+
+}  // extern "C"

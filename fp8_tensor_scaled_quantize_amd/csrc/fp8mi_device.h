@@ -1,0 +1,183 @@
+// Device-side building blocks shared by the quantize, fold and GEMM kernels:
+// fp8 encode, bf16 rounding, wave/block reductions and the ring fold.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mi {
+
+enum Fmt : int { kE4M3 = 0, kE5M2 = 1 };
+enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+template <int FMT> struct FmtTraits;
+// OCP E4M3FN: largest finite 448 (S.1111.110); E5M2: 57344 (S.11110.11).
+template <> struct FmtTraits<kE4M3> { static constexpr float kMax = 448.0f; };
+template <> struct FmtTraits<kE5M2> { static constexpr float kMax = 57344.0f; };
+
+// ---------------------------------------------------------------------------
+// Input element types, widened exactly to fp32.
+// ---------------------------------------------------------------------------
+template <int DT> struct In;
+template <> struct In<kF32> { using T = float; static constexpr int kBytes = 4; };
+template <> struct In<kF16> { using T = uint16_t; static constexpr int kBytes = 2; };
+template <> struct In<kBF16> { using T = uint16_t; static constexpr int kBytes = 2; };
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+  return (float)v;  // exact (v_cvt_f32_f16)
+}
+
+// Element widening from a 32-bit word holding two 16-bit values (lo = first).
+template <int DT> __device__ __forceinline__ void widen2(uint32_t w, float& a, float& b) {
+  if constexpr (DT == kBF16) {
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xFFFF0000u);
+  } else {
+    a = f16_to_f32(w & 0xFFFFu);
+    b = f16_to_f32(w >> 16);
+  }
+}
+
+// Load one element (any alignment of its own size).
+template <int DT> __device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  if constexpr (DT == kF32) return static_cast<const float*>(base)[idx];
+  else if constexpr (DT == kBF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  else return f16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 encode.  The fast path clamps to +-fmt_max with v_med3 and converts with
+// v_cvt_pk_{fp8,bf8}_f32 (round to nearest even; exact for every non-NaN fp32
+// input once clamped).  NaN inputs take enc_exact, which gives the NaN code
+// 0x7F with the input's sign.
+// ---------------------------------------------------------------------------
+template <int FMT> __device__ __forceinline__ float clampf(float v) {
+  constexpr float m = FmtTraits<FMT>::kMax;
+  return __builtin_amdgcn_fmed3f(v, -m, m);
+}
+
+// Four values -> one word, element j in byte j.
+template <int FMT> __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  int w;
+  if constexpr (FMT == kE4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clampf<FMT>(a), clampf<FMT>(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clampf<FMT>(c), clampf<FMT>(d), w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(clampf<FMT>(a), clampf<FMT>(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(clampf<FMT>(c), clampf<FMT>(d), w, true);
+  }
+  return (uint32_t)w;
+}
+
+// Integer saturating round-to-nearest-even encoder, used for words that hold
+// a NaN.  Normal range: drop the low fp32 mantissa bits with RNE (a carry
+// moves into the exponent field exactly as the format's code order does);
+// subnormal range: the code is the value in units of the smallest subnormal,
+// rounded to nearest even.
+template <int FMT> __device__ __forceinline__ uint32_t enc_exact(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t s = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu | s;
+  if constexpr (FMT == kE4M3) {
+    if (a >= 0x43E00000u) return 0x7Eu | s;                  // >= 448
+    if (a < 0x3C800000u)                                     // < 2^-6
+      return (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f) | s;
+    uint32_t c = (a >> 20) - (120u << 3);
+    const uint32_t rem = a & 0xFFFFFu;
+    c += (rem > 0x80000u) || (rem == 0x80000u && (c & 1u));
+    return c | s;
+  } else {
+    if (a >= 0x47600000u) return 0x7Bu | s;                  // >= 57344
+    if (a < 0x38800000u)                                     // < 2^-14
+      return (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f) | s;
+    uint32_t c = (a >> 21) - (112u << 2);
+    const uint32_t rem = a & 0x1FFFFFu;
+    c += (rem > 0x100000u) || (rem == 0x100000u && (c & 1u));
+    return c | s;
+  }
+}
+
+template <int FMT> __device__ __forceinline__ uint32_t enc4_exact(float a, float b, float c, float d) {
+  return enc_exact<FMT>(a) | (enc_exact<FMT>(b) << 8) | (enc_exact<FMT>(c) << 16) | (enc_exact<FMT>(d) << 24);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 round to nearest even from fp32 (overflow to inf, NaN kept quiet).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Reductions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Max over the block; the result is valid in every thread.  `red` holds one
+// float per wave.
+template <int NT> __device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Ring fold: write amax into hist[slot], advance the slot modulo H, publish
+// fmt_max / max(hist) (1.0 when that maximum is 0 or not finite, or the
+// quotient is not a finite positive number).  Runs in one thread.
+// ---------------------------------------------------------------------------
+template <int FMT> __device__ void ring_fold(uint32_t* ring, int H, float amax) {
+  float* hist = reinterpret_cast<float*>(ring);
+  uint32_t slot = ring[H + 1] % (uint32_t)H;
+  hist[slot] = amax;
+  slot = (slot + 1u == (uint32_t)H) ? 0u : slot + 1u;
+  float m = hist[0];
+  for (int i = 1; i < H; ++i) m = fmaxf(m, hist[i]);
+  float s = 1.0f;
+  if (m > 0.0f && m <= 3.40282347e38f) {
+    const float q = FmtTraits<FMT>::kMax / m;  // IEEE division
+    if (q > 0.0f && q <= 3.40282347e38f) s = q;
+  }
+  ring[H] = __float_as_uint(s);
+  ring[H + 1] = slot;
+}
+
+// End of a ring-mode quantize workgroup: publish this block's amax into the
+// ring's accumulator and take a ticket; the block that takes the last ticket
+// folds the accumulated amax into the ring, writes the outputs that belong to
+// the whole call and re-arms ticket and accumulator.  Thread 0 only.
+//
+// Ordering: the amax max and the ticket are device-scope atomics; the ticket
+// add is acq_rel, so every block's accumulator update happens-before the last
+// block's read of it, across all XCDs.
+template <int FMT>
+__device__ void ring_block_done(uint32_t* ring, int H, float block_amax, float s_used,
+                                float* scale_inv_out, float* amax_out) {
+  uint32_t* ticket = ring + H + 2;
+  uint32_t* acc = ring + H + 3;
+  __hip_atomic_fetch_max(acc, __float_as_uint(block_amax), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t nblk = gridDim.x * gridDim.y * gridDim.z;
+  const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (t != nblk - 1u) return;
+  const float a = __uint_as_float(__hip_atomic_load(acc, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
+  if (scale_inv_out) *scale_inv_out = 1.0f / s_used;
+  if (amax_out) *amax_out = a;
+  ring_fold<FMT>(ring, H, a);
+  __hip_atomic_store(acc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(ticket, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace fp8mi

@@ -1,0 +1,33 @@
+// Host-side internal interface between the C ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mi {
+
+// Compute-unit count of the current device (cached per device).
+int device_cu_count();
+
+// mode: 0 row, 1 transposed, 2 dual.  Arguments already validated.
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt, int mode,
+                           uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t, const float* scale,
+                           uint32_t* ring, int H, float* scale_inv_out, float* amax_out, hipStream_t st);
+
+hipError_t launch_amax_fold(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st);
+
+struct MmArgs {
+  const uint8_t* a;
+  const uint8_t* b;
+  int64_t lda, ldb, stride_a, stride_b;
+  int64_t M, N, K, batch;
+  const float* a_scale_inv;
+  const float* b_scale_inv;
+  const void* bias;
+  int bias_dtype;  // -1: no bias
+  uint16_t* c;
+  int64_t ldc, stride_c;
+};
+
+hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+
+}  // namespace fp8mi

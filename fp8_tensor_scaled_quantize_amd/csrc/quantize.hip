@@ -1,0 +1,367 @@
+// Per-tensor scaled fp8 quantize for gfx950: row, transposed and dual layouts,
+// raw-value amax and the in-kernel ring fold.
+//
+// log:csrc/kernels/fp8/quantize.cuh (the tiled transposed quantize commit):
+// one tiled kernel serves the transposed layout ("layout 1") and the dual
+// layout ("layout 2"), handling odd widths and misaligned bases inside the
+// kernel; the elementwise (row) quantize is a separate streaming kernel.
+// log:tests/extension (the in-kernel ring fold commit): the last workgroup
+// folds amax into the history window and publishes the next scale.
+// log:csrc/kernels/fp8_mm.cu, commit 69f35c46e0: amax is taken from the raw
+// input, never from the scaled or encoded values.
+//
+// MI355X shape of the kernels (not the pages' sm_89 one):
+//  * quantize_flat: contiguous row layout; each wave moves 64 x 16-byte loads
+//    per step (one contiguous 1 KiB segment per load instruction) and writes
+//    one contiguous segment of codes per store instruction.
+//  * quantize_tiled: 128-row x 64-column tiles, 256 threads.  Each thread
+//    loads a 4-row x 8-column micro block (16-byte loads where aligned), so
+//    the row-layout codes leave straight from registers and the transposed
+//    codes need only a 4x4 byte transpose in registers plus one 8 KiB LDS
+//    pass, after which every lane stores 16 contiguous bytes of a transposed
+//    row (128-byte segments per 8 lanes).
+//  * amax: wave shuffle reduction, one device-scope atomic max per workgroup.
+#include "fp8mi_device.h"
+#include "fp8mi_internal.h"
+
+namespace fp8mi {
+
+struct QuantArgs {
+  const void* x;
+  int64_t rows, cols, ld_x;
+  uint8_t* out_row;
+  int64_t ld_row;
+  uint8_t* out_t;
+  int64_t ld_t;
+  const float* scale;   // explicit scale, or null with a ring
+  uint32_t* ring;       // ring buffer, or null
+  int H;
+  float* scale_inv_out;
+  float* amax_out;
+};
+
+// Shared ending of every quantize workgroup.
+template <int FMT, int NT>
+__device__ __forceinline__ void quant_block_done(const QuantArgs& p, float thread_amax, float s, float* red) {
+  const float bmax = block_max<NT>(thread_amax, red);
+  if (threadIdx.x != 0) return;
+  if (p.ring) {
+    ring_block_done<FMT>(p.ring, p.H, bmax, s, p.scale_inv_out, p.amax_out);
+  } else {
+    if (p.amax_out)
+      __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(p.amax_out), __float_as_uint(bmax), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    if (p.scale_inv_out && blockIdx.x == 0 && blockIdx.y == 0) *p.scale_inv_out = 1.0f / s;
+  }
+}
+
+// max |v| over the non-NaN values.  The fast loops use v_max_f32, which is
+// not NaN-free when an operand is a signalling NaN (it returns a quiet NaN),
+// so a chunk that holds any NaN recomputes its amax here.
+template <int N> __device__ __forceinline__ float nan_free_absmax(const float* f) {
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    if (f[e] == f[e]) m = fmaxf(m, fabsf(f[e]));
+  return m;
+}
+
+template <int FMT> __device__ __forceinline__ float read_scale(const QuantArgs& p) {
+  return p.ring ? __uint_as_float(p.ring[p.H]) : *p.scale;
+}
+
+// ===========================================================================
+// Row layout, contiguous input and output (ld == cols), 16-byte aligned bases.
+// A "wave step" covers 64 lanes x 16 elements; a lane holds NL 16-byte loads
+// whose element offsets are (j * 64 + lane) * EPL within the step.
+// ===========================================================================
+constexpr int kFlatThreads = 256;
+constexpr int kFlatElemsPerThread = 16;
+constexpr int kFlatWaveStep = 64 * kFlatElemsPerThread;                   // 1024 elements
+constexpr int kFlatBlockStep = kFlatThreads * kFlatElemsPerThread;      // 4096 elements
+
+template <int DT, int FMT>
+__global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64_t n, int64_t steps_per_block) {
+  __shared__ float red[kFlatThreads / 64];
+  constexpr int EB = In<DT>::kBytes;
+  constexpr int EPL = 16 / EB;                   // elements per 16-byte load
+  constexpr int NL = kFlatElemsPerThread / EPL;  // loads per lane per step
+  const float s = read_scale<FMT>(p);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  float amax = 0.0f;
+  const char* xb = static_cast<const char*>(p.x);
+  const int64_t first = (int64_t)blockIdx.x * steps_per_block;
+  const int64_t total_steps = (n + kFlatBlockStep - 1) / kFlatBlockStep;
+  const int64_t last = first + steps_per_block < total_steps ? first + steps_per_block : total_steps;
+  for (int64_t st = first; st < last; ++st) {
+    const int64_t w0 = st * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
+    if (w0 + kFlatWaveStep <= n) {
+      uint4 v[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        v[j] = *reinterpret_cast<const uint4*>(xb + (w0 + (int64_t)(j * 64 + lane) * EPL) * EB);
+      float f[kFlatElemsPerThread];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        if constexpr (DT == kF32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[j * 4 + e] = __uint_as_float(w[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) widen2<DT>(w[e], f[j * 8 + 2 * e], f[j * 8 + 2 * e + 1]);
+        }
+      }
+      bool nan = false;
+      float camax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kFlatElemsPerThread; ++e) {
+        camax = fmaxf(camax, fabsf(f[e]));
+        nan |= f[e] != f[e];
+      }
+      if (nan) camax = nan_free_absmax<kFlatElemsPerThread>(f);
+      amax = fmaxf(amax, camax);
+      uint32_t code[kFlatElemsPerThread / 4];
+      if (!nan) {
+#pragma unroll
+        for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
+          code[q] = cvt4<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
+      } else {
+#pragma unroll
+        for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
+          code[q] = enc4_exact<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
+      }
+      // store: load j's EPL codes go to out[w0 + (j*64+lane)*EPL ...]
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        uint8_t* o = p.out_row + w0 + (int64_t)(j * 64 + lane) * EPL;
+        if constexpr (EPL == 8) *reinterpret_cast<uint2*>(o) = make_uint2(code[2 * j], code[2 * j + 1]);
+        else *reinterpret_cast<uint32_t*>(o) = code[j];
+      }
+    } else if (w0 < n) {
+      // ragged end of the tensor: element by element, same lane mapping
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const int64_t idx = w0 + (int64_t)(j * 64 + lane) * EPL + e;
+          if (idx < n) {
+            const float xv = load1<DT>(p.x, idx);
+            if (xv == xv) amax = fmaxf(amax, fabsf(xv));
+            p.out_row[idx] = (uint8_t)enc_exact<FMT>(xv * s);
+          }
+        }
+      }
+    }
+  }
+  quant_block_done<FMT, kFlatThreads>(p, amax, s, red);
+}
+
+// ===========================================================================
+// Tiled kernel: transposed, dual, and row layout for strided / misaligned /
+// odd-width inputs.  Tile = 128 rows x 64 columns, 256 threads.
+// Thread t: column group cg = t % 8 (columns 8cg..8cg+7), row group
+// rg = t / 8 (rows 4rg..4rg+3).
+// LDS (transposed codes): 64 columns x 32 words; word w of column c holds
+// rows 4w..4w+3 and sits at c*32 + (w ^ (8 * ((c / 8) & 3))).
+// ===========================================================================
+constexpr int kTileR = 128, kTileC = 64, kTileThreads = 256;
+enum Mode : int { kRow = 0, kTrans = 1, kDual = 2 };
+
+__device__ __forceinline__ int lds_t_index(int c, int w) { return c * 32 + (w ^ (8 * ((c >> 3) & 3))); }
+
+template <int DT, int FMT, int MODE>
+__global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int64_t tiles_c, int64_t ntiles,
+                                                                int64_t tiles_per_block) {
+  __shared__ float red[kTileThreads / 64];
+  __shared__ __align__(16) uint32_t lds_t[(MODE == kRow) ? 1 : kTileC * 32];
+  constexpr int EB = In<DT>::kBytes;
+  const float s = read_scale<FMT>(p);
+  const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
+  float amax = 0.0f;
+  const char* xb = static_cast<const char*>(p.x);
+  const int64_t t_first = (int64_t)blockIdx.x * tiles_per_block;
+  const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
+  for (int64_t tile = t_first; tile < t_last; ++tile) {
+    const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
+    const int64_t cc = c0 + 8 * cg;  // this thread's first column
+    float f[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * rg + i;
+      const char* src = xb + (r * p.ld_x + cc) * EB;
+      const bool full = r < p.rows && cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+      if (full) {
+        if constexpr (DT == kF32) {
+          const uint4 a = reinterpret_cast<const uint4*>(src)[0];
+          const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+          f[i][0] = __uint_as_float(a.x); f[i][1] = __uint_as_float(a.y);
+          f[i][2] = __uint_as_float(a.z); f[i][3] = __uint_as_float(a.w);
+          f[i][4] = __uint_as_float(b.x); f[i][5] = __uint_as_float(b.y);
+          f[i][6] = __uint_as_float(b.z); f[i][7] = __uint_as_float(b.w);
+        } else {
+          const uint4 a = *reinterpret_cast<const uint4*>(src);
+          widen2<DT>(a.x, f[i][0], f[i][1]); widen2<DT>(a.y, f[i][2], f[i][3]);
+          widen2<DT>(a.z, f[i][4], f[i][5]); widen2<DT>(a.w, f[i][6], f[i][7]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          f[i][e] = (r < p.rows && cc + e < p.cols) ? load1<DT>(p.x, r * p.ld_x + cc + e) : 0.0f;
+      }
+    }
+    bool nan = false;
+    float camax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        camax = fmaxf(camax, fabsf(f[i][e]));
+        nan |= f[i][e] != f[i][e];
+      }
+    if (nan) camax = nan_free_absmax<32>(&f[0][0]);
+    amax = fmaxf(amax, camax);
+    uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
+    if (!nan) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          rw[i][h] = cvt4<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s, f[i][4 * h + 3] * s);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          rw[i][h] = enc4_exact<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
+                                     f[i][4 * h + 3] * s);
+    }
+
+    if constexpr (MODE == kRow || MODE == kDual) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + 4 * rg + i;
+        if (r >= p.rows) continue;
+        uint8_t* dst = p.out_row + r * p.ld_row + cc;
+        if (cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(rw[i][0], rw[i][1]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (cc + e < p.cols) dst[e] = (uint8_t)(rw[i][e >> 2] >> (8 * (e & 3)));
+        }
+      }
+    }
+
+    if constexpr (MODE == kTrans || MODE == kDual) {
+      // 4x8 bytes -> 8 column words (rows 4rg..4rg+3 of column 8cg+e)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int h = e >> 2, sh = 8 * (e & 3);
+        const uint32_t col = ((rw[0][h] >> sh) & 0xFFu) | (((rw[1][h] >> sh) & 0xFFu) << 8) |
+                             (((rw[2][h] >> sh) & 0xFFu) << 16) | (((rw[3][h] >> sh) & 0xFFu) << 24);
+        lds_t[lds_t_index(8 * cg + e, rg)] = col;
+      }
+      __syncthreads();
+      // 64 transposed rows (one per input column) x 128 bytes; lane: row cl, 16 bytes at 16q
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int cl = (t >> 3) + 32 * pass, q = t & 7;
+        const int64_t c = c0 + cl;
+        const int64_t rr = r0 + 16 * q;
+        if (c < p.cols && rr < p.rows) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&lds_t[lds_t_index(cl, 4 * q)]);
+          uint8_t* dst = p.out_t + c * p.ld_t + rr;
+          if (rr + 16 <= p.rows && ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0)) {
+            *reinterpret_cast<uint4*>(dst) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (rr + e < p.rows) dst[e] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+          }
+        }
+      }
+      __syncthreads();  // LDS reused by the next tile
+    }
+  }
+  quant_block_done<FMT, kTileThreads>(p, amax, s, red);
+}
+
+// Fold alone / arming of a ring-less amax output.
+template <int FMT> __global__ void amax_fold_kernel(uint32_t* ring, int H, const float* amax) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) ring_fold<FMT>(ring, H, *amax);
+}
+__global__ void zero_word_kernel(float* p) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0.0f;
+}
+
+// ===========================================================================
+// Host launchers.
+// ===========================================================================
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <int DT, int FMT>
+static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
+  const int ncu = device_cu_count();
+  const int64_t n = p.rows * p.cols;
+  const bool contiguous_row = mode == kRow && p.ld_x == p.cols && p.ld_row == p.cols &&
+                              (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
+                              (reinterpret_cast<uintptr_t>(p.out_row) & 15u) == 0;
+  if (contiguous_row || n == 0) {
+    const int64_t steps = cdiv(n, kFlatBlockStep);
+    const int64_t max_blocks = (int64_t)ncu * 8;
+    const int64_t spb = steps <= max_blocks ? 1 : cdiv(steps, max_blocks);
+    const int64_t blocks = steps == 0 ? 1 : cdiv(steps, spb);
+    hipLaunchKernelGGL((quantize_flat<DT, FMT>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n, spb);
+    return hipGetLastError();
+  }
+  const int64_t tiles_c = cdiv(p.cols, kTileC);
+  const int64_t ntiles = cdiv(p.rows, kTileR) * tiles_c;
+  const int64_t max_blocks = (int64_t)ncu * 8;
+  const int64_t tpb = ntiles <= max_blocks ? 1 : cdiv(ntiles, max_blocks);
+  const int64_t blocks = cdiv(ntiles, tpb);
+  switch (mode) {
+    case kRow:
+      hipLaunchKernelGGL((quantize_tiled<DT, FMT, kRow>), dim3((unsigned)blocks), dim3(kTileThreads), 0, st, p,
+                         tiles_c, ntiles, tpb);
+      break;
+    case kTrans:
+      hipLaunchKernelGGL((quantize_tiled<DT, FMT, kTrans>), dim3((unsigned)blocks), dim3(kTileThreads), 0, st, p,
+                         tiles_c, ntiles, tpb);
+      break;
+    default:
+      hipLaunchKernelGGL((quantize_tiled<DT, FMT, kDual>), dim3((unsigned)blocks), dim3(kTileThreads), 0, st, p,
+                         tiles_c, ntiles, tpb);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT> static hipError_t launch_fmt(const QuantArgs& p, int dt, int mode, hipStream_t st) {
+  switch (dt) {
+    case kF32: return launch_dt_fmt<kF32, FMT>(p, mode, st);
+    case kF16: return launch_dt_fmt<kF16, FMT>(p, mode, st);
+    default: return launch_dt_fmt<kBF16, FMT>(p, mode, st);
+  }
+}
+
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt, int mode,
+                           uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t, const float* scale,
+                           uint32_t* ring, int H, float* scale_inv_out, float* amax_out, hipStream_t st) {
+  QuantArgs p{x, rows, cols, ld_x, out_row, ld_row, out_t, ld_t, scale, ring, H, scale_inv_out, amax_out};
+  if (!ring && amax_out) {
+    hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, st, amax_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return fmt == kE4M3 ? launch_fmt<kE4M3>(p, dt, mode, st) : launch_fmt<kE5M2>(p, dt, mode, st);
+}
+
+hipError_t launch_amax_fold(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st) {
+  if (fmt == kE4M3) hipLaunchKernelGGL(amax_fold_kernel<kE4M3>, dim3(1), dim3(64), 0, st, ring, H, amax);
+  else hipLaunchKernelGGL(amax_fold_kernel<kE5M2>, dim3(1), dim3(64), 0, st, ring, H, amax);
+  return hipGetLastError();
+}
+
+}  // namespace fp8mi

@@ -1,0 +1,166 @@
+/*
+ * fp8mi -- FP8 per-tensor scaled quantize, delayed-scaling amax history fold
+ * and per-tensor-scaled fp8 GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named "device" is a device (HBM) pointer;
+ * every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ * NULL = the null stream) and allocates no memory.  The caller owns every
+ * buffer.  Arguments are checked before anything is launched: a call that
+ * returns a status other than FP8MI_OK has written nothing.  A HIP launch
+ * failure returns FP8MI_ERR_HIP; fp8mi_last_error() then holds the HIP text.
+ *
+ * Citations are to the AstrAI commit-log pages (Gitea, ViperEkura/AstrAI);
+ * "log:<path>" names the commit history page of that path.
+ *
+ * Number formats.  OCP FP8: E4M3 (E4M3FN: bias 7, no infinity, S.1111.111 is
+ * NaN, largest 448) and E5M2 (bias 15, largest 57344).  Quantizing x with
+ * per-tensor scale s stores enc(fl32(fl32(x) * s)): the input is widened
+ * exactly to fp32, multiplied once in fp32 (round to nearest even, no flush
+ * of subnormals) and encoded with saturating round-to-nearest-even (ties to
+ * the even code; |v| >= fmt max and +-inf give +-max; NaN gives the format's
+ * NaN code 0x7F with the input's sign; the sign of zero is kept).  Codes are
+ * stored one byte per element, element j of a row at byte j (log:tests/extension,
+ * the commit that fixes fp8 packing of four codes per 32-bit word).
+ *
+ * Amax.  max |fl32(x)| over the raw, unscaled input, NaN ignored
+ * (log:csrc/kernels/fp8_mm.cu, commit 69f35c46e0).
+ *
+ * Ring (delayed scaling; log:tests/extension, the commits that pack
+ * [history | scale | counter] into one device buffer and fold it in the
+ * quantize kernel's last block).  A ring is H + 4 32-bit device words:
+ *   [0, H)  amax history, fp32
+ *   H       current scale, fp32 (the scale the next quantize call uses)
+ *   H+1     next history slot, uint32 in [0, H)
+ *   H+2     completion ticket, uint32, 0 at rest
+ *   H+3     amax accumulator (fp32 bits as uint32), 0 at rest
+ * The caller initialises it (history 0, slot 0, ticket 0, accumulator 0,
+ * scale = a starting scale) and may copy it to checkpoint / restore.  A fold
+ * of amax a writes a into hist[slot], advances slot modulo H, and publishes
+ * scale = fmt_max / max(hist) -- or 1.0 when that maximum is 0 or not finite
+ * or the quotient is not a finite positive number.  After every call the
+ * ticket and accumulator are 0 again.  One ring may be used by at most one
+ * call in flight at a time.
+ */
+#ifndef FP8MI_H
+#define FP8MI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define FP8MI_API __attribute__((visibility("default")))
+#else
+#define FP8MI_API
+#endif
+
+typedef enum {
+  FP8MI_OK = 0,
+  FP8MI_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  FP8MI_ERR_ENUM = 2,        /* format / dtype value out of range                */
+  FP8MI_ERR_SHAPE = 3,       /* negative size, ld smaller than the row, bad H    */
+  FP8MI_ERR_STRIDE = 4,      /* batch strides that overlap written outputs       */
+  FP8MI_ERR_UNSUPPORTED = 5, /* valid request outside the implemented fast path  */
+  FP8MI_ERR_HIP = 6,         /* HIP runtime reported an error                     */
+  FP8MI_ERR_ARG = 7          /* inconsistent optional arguments (scale vs ring)   */
+} fp8mi_status;
+
+typedef enum { FP8MI_E4M3 = 0, FP8MI_E5M2 = 1 } fp8mi_format;
+typedef enum { FP8MI_F32 = 0, FP8MI_F16 = 1, FP8MI_BF16 = 2 } fp8mi_dtype;
+
+/* Largest history window a ring may have. */
+#define FP8MI_MAX_HIST 4096
+
+/*
+ * fp8_quantize -- per-tensor scaled cast of a [rows, cols] tensor to fp8 in
+ * row or transposed layout (log:tests/extension, the commit that splits the
+ * bindings into quantize(transposed) / quantize_dual with a layout enum;
+ * log:csrc/kernels/fp8/quantize.cuh, the commit introducing the tiled
+ * transposed quantize that handles odd widths and misaligned bases in-kernel).
+ *
+ *   x          device, element (i, j) at x[i * ld_x + j]; dtype x_dtype.
+ *              Any element alignment; ld_x >= cols.
+ *   fmt        FP8MI_E4M3 or FP8MI_E5M2.
+ *   transposed 0: out[i * ld_out + j] = q(i, j), ld_out >= cols;
+ *              1: out[j * ld_out + i] = q(i, j), ld_out >= rows.
+ *              Bytes of `out` outside the rows x cols codes are not written.
+ *   scale      device fp32 per-tensor scale, or NULL;
+ *   ring       device ring of hist_len + 4 words, or NULL.  Exactly one of
+ *              scale / ring is given (else FP8MI_ERR_ARG).  With a ring the
+ *              call uses the ring's current scale and its last workgroup folds
+ *              this call's amax into the ring (the next scale is published
+ *              on device; no host round trip).
+ *   scale_inv_out  optional device fp32: 1 / (the scale this call used),
+ *              i.e. the dequantisation multiplier for fp8_mm -- a snapshot
+ *              taken before the fold replaces the ring's scale
+ *              (log:tests/extension, the commit snapshotting sx/sw/sg).
+ *   amax_out   optional device fp32: this call's raw amax.
+ * rows * cols == 0 is a valid no-op for the codes; a ring still folds amax 0.
+ */
+FP8MI_API fp8mi_status fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                          int fmt, int transposed, uint8_t* out, int64_t ld_out,
+                          const float* scale, uint32_t* ring, int32_t hist_len,
+                          float* scale_inv_out, float* amax_out, void* stream);
+
+/*
+ * fp8_quantize_dual -- one read of x, both layouts written: out_row (as
+ * transposed = 0) and out_t (as transposed = 1); one amax, one fold
+ * (log:csrc/kernels/fp8/quantize.cuh, the dual-layout "layout 2" of the
+ * tiled quantize commit).  Arguments as fp8_quantize.
+ */
+FP8MI_API fp8mi_status fp8_quantize_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                               int fmt, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
+                               const float* scale, uint32_t* ring, int32_t hist_len,
+                               float* scale_inv_out, float* amax_out, void* stream);
+
+/*
+ * fp8_amax_fold -- the ring fold alone, for an amax already on the device
+ * (e.g. one reduced over several devices): one tiny launch that performs
+ * exactly the fold a ring-mode quantize performs in its last workgroup
+ * (log:tests/extension, the commit testing the in-kernel fold against a host
+ * reference).  ring: device, hist_len + 4 words; amax: device fp32.
+ */
+FP8MI_API fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const float* amax, int fmt, void* stream);
+
+/*
+ * fp8_mm -- per-tensor-scaled fp8 GEMM, NT operands, bf16 output
+ * (log:tests/extension: the commits fusing the fp32 bias ahead of a single
+ * bf16 rounding, accepting 3-D operands through batch strides with stride-0
+ * broadcast, and making the output always bf16; log:csrc/kernels/fp8_mm.cu,
+ * commit 5244f1a8fc, per-tensor A/B scales applied inside the GEMM).
+ *
+ *   C[b,i,j] = bf16( fl32( sum_k dec(A[b,i,k]) * dec(B[b,j,k]) ) * fl32(sa * sb)
+ *                    + bias[j] )      -- accumulated in fp32, one rounding.
+ *   A(b,i,k) = a[b * stride_a + i * lda + k]   (fmt_a codes, device)
+ *   B(b,j,k) = b[b * stride_b + j * ldb + k]   (fmt_b codes, device)
+ *   C(b,i,j) = c[b * stride_c + i * ldc + j]   (bf16, device)
+ *   stride_a / stride_b may be 0 (one operand broadcast over the batch).
+ *   a_scale_inv, b_scale_inv: device fp32 dequantisation multipliers
+ *   (e.g. scale_inv_out of the quantize calls), NULL meaning 1.0.
+ *   bias: device [N] of bias_dtype (FP8MI_F32 / FP8MI_F16 / FP8MI_BF16), one
+ *   vector shared by every row and batch; NULL for no bias.
+ * Requirements: a, b 16-byte aligned; lda, ldb, K multiples of 16 (else
+ * FP8MI_ERR_UNSUPPORTED); lda, ldb >= K; ldc >= N; c 2-byte aligned; with
+ * batch > 1, stride_c >= M * ldc.  M, N or batch 0: no-op.  K == 0 writes
+ * bf16(bias) (or zeros).
+ */
+FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a,
+                    const uint8_t* b, int fmt_b, int64_t ldb, int64_t stride_b,
+                    int64_t M, int64_t N, int64_t K, int64_t batch,
+                    const float* a_scale_inv, const float* b_scale_inv,
+                    const void* bias, int bias_dtype,
+                    void* c, int64_t ldc, int64_t stride_c, void* stream);
+
+/* Static text of a status code. */
+FP8MI_API const char* fp8mi_status_string(int status);
+/* Thread-local detail of the last non-OK status returned on this thread. */
+FP8MI_API const char* fp8mi_last_error(void);
+/* Library version, e.g. "fp8mi 0.1 gfx950". */
+FP8MI_API const char* fp8mi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8MI_H */

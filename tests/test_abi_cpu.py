@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every symbol include/fp8mi.h declares,
+and rejects invalid arguments with the documented status before touching the
+GPU (these calls never reach a HIP API, so they run without a device)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mi.h")
+
+fp8mi = pytest.importorskip("fp8_tensor_scaled_quantize_amd")
+from fp8_tensor_scaled_quantize_amd import _lib  # noqa: E402
+
+OK, NULL, ENUM, SHAPE, STRIDE, UNSUP, HIP, ARG = range(8)
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"FP8MI_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfp8mi.so not built")
+    return _lib.lib()
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(names) == {"fp8_quantize", "fp8_quantize_dual", "fp8_amax_fold", "fp8_mm",
+                          "fp8mi_status_string", "fp8mi_last_error", "fp8mi_version"} | set(
+        n for n in names if n.startswith("fp8_"))
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_status_strings(L):
+    assert L.fp8mi_version().decode().startswith("fp8mi")
+    for s in range(8):
+        assert L.fp8mi_status_string(s).decode()
+    assert L.fp8mi_status_string(99) == b"unknown status"
+
+
+def q(L, x=FAKE, dt=2, rows=4, cols=4, ld=4, fmt=0, tr=0, out=FAKE, ld_out=4, scale=FAKE, ring=None, H=0,
+      sinv=None, amax=None):
+    return L.fp8_quantize(x, dt, rows, cols, ld, fmt, tr, out, ld_out, scale, ring, H, sinv, amax, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=3), ENUM), (dict(dt=-1), ENUM), (dict(fmt=2), ENUM), (dict(tr=2), ENUM),
+    (dict(rows=-1), SHAPE), (dict(cols=-5), SHAPE), (dict(ld=3), SHAPE),
+    (dict(x=None), NULL), (dict(out=None), NULL),
+    (dict(ld_out=3), SHAPE), (dict(tr=1, rows=8, ld_out=7), SHAPE),
+    (dict(scale=None), ARG), (dict(ring=FAKE, H=4), ARG),
+    (dict(scale=None, ring=FAKE, H=0), SHAPE), (dict(scale=None, ring=FAKE, H=5000), SHAPE),
+    (dict(x=FAKE + 1), ARG), (dict(scale=FAKE + 2), ARG), (dict(amax=FAKE + 1), ARG),
+])
+def test_quantize_rejects(L, kw, status):
+    assert q(L, **kw) == status
+    assert L.fp8mi_last_error()
+
+
+def test_quantize_dual_rejects(L):
+    f = L.fp8_quantize_dual
+    assert f(FAKE, 2, 4, 4, 4, 0, None, 4, FAKE, 4, FAKE, None, 0, None, None, None) == NULL
+    assert f(FAKE, 2, 4, 4, 4, 0, FAKE, 4, None, 4, FAKE, None, 0, None, None, None) == NULL
+    assert f(FAKE, 2, 4, 8, 8, 0, FAKE, 8, FAKE, 3, FAKE, None, 0, None, None, None) == SHAPE
+    assert f(FAKE, 2, 4, 4, 4, 1, FAKE, 4, FAKE, 4, None, None, 0, None, None, None) == ARG
+
+
+def test_amax_fold_rejects(L):
+    assert L.fp8_amax_fold(None, 4, FAKE, 0, None) == NULL
+    assert L.fp8_amax_fold(FAKE, 4, None, 0, None) == NULL
+    assert L.fp8_amax_fold(FAKE, 4, FAKE, 9, None) == ENUM
+    assert L.fp8_amax_fold(FAKE, 0, FAKE, 0, None) == SHAPE
+
+
+def mm(L, a=FAKE, fa=0, lda=64, sa=0, b=FAKE, fb=0, ldb=64, sb=0, M=32, N=32, K=64, batch=1, sai=None, sbi=None,
+       bias=None, bdt=2, c=FAKE, ldc=32, sc=0):
+    return L.fp8_mm(a, fa, lda, sa, b, fb, ldb, sb, M, N, K, batch, sai, sbi, bias, bdt, c, ldc, sc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fa=2), ENUM), (dict(fb=-1), ENUM), (dict(bias=FAKE, bdt=5), ENUM),
+    (dict(M=-1), SHAPE), (dict(K=-16), SHAPE), (dict(batch=-1), SHAPE),
+    (dict(c=None), NULL), (dict(a=None), NULL), (dict(b=None), NULL),
+    (dict(ldc=31), SHAPE), (dict(lda=48), SHAPE), (dict(ldb=32), SHAPE),
+    (dict(batch=2, sc=32 * 31), STRIDE), (dict(sa=-64), STRIDE),
+    (dict(c=FAKE + 1), ARG), (dict(bias=FAKE + 2, bdt=0), ARG),
+    (dict(K=40, lda=64, ldb=64), UNSUP), (dict(lda=72, K=64), UNSUP), (dict(a=FAKE + 8), UNSUP),
+    (dict(batch=2, sa=8, sc=32 * 32), UNSUP), (dict(batch=70000, sc=32 * 32), UNSUP),
+])
+def test_mm_rejects(L, kw, status):
+    assert mm(L, **kw) == status
+
+
+def test_mm_empty_is_noop(L):
+    # no pointer is touched for an empty problem
+    assert mm(L, M=0, a=None, b=None, c=None) == OK
+    assert mm(L, N=0, a=None, b=None, c=None) == OK
+    assert mm(L, batch=0, a=None, b=None, c=None) == OK
+
+
+def test_binding_raises_without_gpu_on_bad_args():
+    import torch
+    x = torch.zeros(4, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fp8mi.fp8_quantize(x.t()[:, :3].t() if False else x.unsqueeze(0), fp8mi.E4M3, scale=None)
+    with pytest.raises(ValueError):
+        fp8mi.fp8_quantize(x, "e9m9", scale=None)

@@ -1,0 +1,271 @@
+"""GPU parity of fp8_mm against the oracle's float64 GEMM rounded once to bf16.
+
+Two kinds of check:
+
+* exact data -- codes whose values are small integers (|v| <= 16 in E4M3,
+  <= 8 in E5M2), power-of-two scales and integer bias: every partial sum is
+  exact both in the MFMA's product groups and in fp32, so the GPU output must
+  equal the oracle's bit for bit.  This pins indexing, tails, batch strides,
+  broadcast and the epilogue with no tolerance at all.
+* quantised Gaussian data -- every output within
+      1 bf16 ulp(|ref|) + 1e-5 * sum_k |a_ik b_jk|          (the stated bound)
+    + 7 * 2^-12 * sum_g max_{k in g} |a_ik| * max_{k in g} |b_jk|
+  where g runs over the aligned groups of 8 consecutive k.  The last term is
+  the documented behaviour of gfx950's fp8 MFMA: it adds the products of each
+  group of 8 after truncating each toward zero to a grid 2^-13 below the
+  group's largest product exponent (measured on the device with isolated
+  products), so one group can lose up to 7 grid steps; that loss is bounded
+  by the group maxima.  At least 99.9 % of the outputs of every large problem
+  must also meet the stated bound alone.
+
+Large problems are checked on a seeded sample of full output rows (each
+sampled row is computed exactly by the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import DEV, np_bf16_bits, scalar
+
+pytestmark = pytest.mark.gpu
+
+fp8mi = pytest.importorskip("fp8_tensor_scaled_quantize_amd")
+FID = {O.E4M3: 0, O.E5M2: 1}
+
+
+def make_codes(shape, fmt, *key):
+    """fp8 codes of quantised N(0,1) data at scale fmt_max / amax."""
+    x = synth.gaussian_f32(shape, 1.0, *key)
+    s = np.float32(O.FMT_MAX[fmt]) / O.amax(x)
+    return O.encode(O.scaled_values(x, s), fmt)
+
+
+def make_int_codes(shape, fmt, *key):
+    """Codes of small integers: |v| <= 16 (E4M3) / <= 8 (E5M2), all exact."""
+    lim = 16 if fmt == O.E4M3 else 8
+    v = synth.rng(*key).integers(-lim, lim + 1, size=shape).astype(np.float32)
+    return O.encode(v, fmt)
+
+
+def to_dev_codes(c):
+    return torch.from_numpy(np.ascontiguousarray(c)).to(DEV)
+
+
+MFMA_GROUP = 8
+MFMA_GROUP_LOSS = 7 * 2.0 ** -12
+
+
+def mfma_group_term(a, fa, b, fb, sa, sb):
+    """7 * 2^-12 * sum_g max|a_ik| max|b_jk| over aligned groups of 8 k."""
+    da = np.abs(O.decode_table(fa)[a])
+    db = np.abs(O.decode_table(fb)[b])
+    K = a.shape[-1]
+    if K == 0:
+        return np.zeros((a.shape[0], b.shape[0]))
+    ga = da.reshape(a.shape[0], K // MFMA_GROUP, MFMA_GROUP).max(-1)
+    gb = db.reshape(b.shape[0], K // MFMA_GROUP, MFMA_GROUP).max(-1)
+    return MFMA_GROUP_LOSS * (ga @ gb.T) * abs(float(np.float32(sa)) * float(np.float32(sb)))
+
+
+def check(gpu_bits, a, fa, b, fb, sa, sb, bias, rows=None, tag="", exact=False):
+    """Compare (a sample of rows of) the GPU output with the oracle."""
+    a3 = a if a.ndim == 3 else a[None]
+    b3 = b if b.ndim == 3 else b[None]
+    g3 = gpu_bits if gpu_bits.ndim == 3 else gpu_bits[None]
+    batch = max(a3.shape[0], b3.shape[0])
+    n_all = n_stated = 0
+    for z in range(batch):
+        az = a3[min(z, a3.shape[0] - 1)]
+        bz = b3[min(z, b3.shape[0] - 1)]
+        rsel = np.arange(az.shape[0]) if rows is None else rows
+        ref, mag = O.mm(az[rsel], fa, bz, fb, sa, sb, bias)
+        got = g3[z][rsel]
+        if exact:
+            bad = got != ref[0]
+            assert not bad.any(), f"{tag} batch {z}: {bad.sum()} of {bad.size} differ from the exact result"
+            continue
+        stated = O.within_tolerance(got, ref[0], mag[0])
+        ext = O.within_tolerance(got, ref[0], mag[0] + mfma_group_term(az[rsel], fa, bz, fb, sa, sb) / 1e-5)
+        assert ext.all(), f"{tag} batch {z}: {(~ext).sum()} of {ext.size} outside tolerance"
+        n_all += stated.size
+        n_stated += int(stated.sum())
+    if not exact and n_all >= 4096:
+        frac = n_stated / n_all
+        assert frac >= 0.999, f"{tag}: only {frac:.5f} of outputs within the stated bound"
+
+
+def sample_rows(M, n, *key):
+    if M <= n:
+        return None
+    return np.sort(synth.rng(*key).choice(M, size=n, replace=False))
+
+
+def run_case(M, N, K, fa=O.E4M3, fb=O.E4M3, bias_kind=None, key=0, sample=64, scales=None):
+    a = make_codes((M, K), fa, 30, key, 0)
+    b = make_codes((N, K), fb, 30, key, 1)
+    if scales is None:
+        sa = synth.loguniform_scale(-4, 4, 30, key, synth.T_ASCALE)
+        sb = synth.loguniform_scale(-4, 4, 30, key, synth.T_BSCALE)
+    else:
+        sa, sb = scales
+    rows = sample_rows(M, sample, 30, key, 9)
+    bias = bias_t = None
+    if bias_kind is not None:
+        # bias sized like the output (so the fp32 add is visible above 1 bf16 ulp)
+        rr = np.arange(min(M, 8))
+        y0, _ = O.mm_exact_f64(a[rr], fa, b, fb, sa, sb)
+        rms = float(np.sqrt(np.mean(y0 ** 2))) or 1.0
+        bv = synth.gaussian_f32((N,), rms, 30, key, synth.T_BIAS)
+        if bias_kind == "f32":
+            bias, bias_t = bv.astype(np.float64), torch.from_numpy(bv).to(DEV)
+        else:
+            bits = synth.f32_to_bf16_bits(bv)
+            bias = O.widen_to_f32(bits, "bf16").astype(np.float64)
+            bias_t = synth.to_torch(bits, "bf16").to(DEV)
+    y = fp8mi.fp8_mm(to_dev_codes(a), to_dev_codes(b), FID[fa], FID[fb], scalar(sa), scalar(sb), bias_t)
+    check(np_bf16_bits(y), a, fa, b, fb, sa, sb, bias, rows, tag=f"{M}x{N}x{K}")
+    return y
+
+
+def test_tiny_config():
+    run_case(64, 256, 256, bias_kind="bf16", key=1)
+
+
+@pytest.mark.parametrize("mnk", [(2048, 1536, 1536), (2048, 6912, 1536), (2048, 1536, 6912)])
+def test_linear_shapes_with_bias(mnk):
+    run_case(*mnk, bias_kind="bf16", key=2 + mnk[1] + mnk[2])
+
+
+@pytest.mark.parametrize("S", [1024, 2048, 4096, 8192])
+@pytest.mark.parametrize("bias", [None, "f32"])
+def test_square_sweep(S, bias):
+    run_case(S, S, S, bias_kind=bias, key=10 + S, sample=48 if S >= 4096 else 128)
+
+
+@pytest.mark.parametrize("mnk", [(64, 8192, 2048), (1024, 1536, 2048), (1024, 1537, 2048)])
+def test_skinny_and_odd_n(mnk):
+    run_case(*mnk, bias_kind="f32", key=20 + mnk[1])
+
+
+@pytest.mark.parametrize("batch,mnk", [(64, (512, 512, 512)), (8, (1024, 2048, 2048))])
+@pytest.mark.parametrize("broadcast_b", [False, True])
+def test_batched(batch, mnk, broadcast_b):
+    M, N, K = mnk
+    a = make_codes((batch, M, K), O.E4M3, 40, batch, 0)
+    b = make_codes((1 if broadcast_b else batch, N, K), O.E4M3, 40, batch, 1)
+    sa, sb = synth.loguniform_scale(-4, 4, 40, 1), synth.loguniform_scale(-4, 4, 40, 2)
+    bv = synth.gaussian_f32((N,), 4.0, 40, batch, 3)
+    ad, bd = to_dev_codes(a), to_dev_codes(b)
+    if broadcast_b:
+        bd = bd.expand(batch, N, K)  # stride 0 over the batch
+    y = fp8mi.fp8_mm(ad, bd, 0, 0, scalar(sa), scalar(sb), torch.from_numpy(bv).to(DEV))
+    rows = sample_rows(M, 16, 40, batch, 4)
+    check(np_bf16_bits(y), a, O.E4M3, b, O.E4M3, sa, sb, bv.astype(np.float64), rows, tag=f"bmm{batch}")
+    if broadcast_b:
+        # stride-0 broadcast == the materialised copy, bit for bit
+        y2 = fp8mi.fp8_mm(ad, bd.contiguous(), 0, 0, scalar(sa), scalar(sb), torch.from_numpy(bv).to(DEV))
+        assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("fa,fb", [(O.E5M2, O.E4M3), (O.E4M3, O.E5M2), (O.E5M2, O.E5M2)])
+def test_mixed_formats(fa, fb):
+    run_case(512, 384, 1024, fa=fa, fb=fb, bias_kind="bf16", key=50 + FID[fa] * 2 + FID[fb])
+
+
+@pytest.mark.parametrize("mnk", [(1, 1, 16), (17, 33, 48), (130, 257, 272), (65, 129, 144), (3, 1000, 32),
+                                 (300, 5, 2064), (129, 64, 128)])
+def test_ragged_edges(mnk):
+    run_case(*mnk, bias_kind="bf16", key=60 + sum(mnk))
+
+
+def test_k_zero_writes_bias():
+    bits = synth.gaussian((37,), 1.0, "bf16", 61, 1)
+    y = fp8mi.fp8_mm(torch.zeros((5, 0), dtype=torch.uint8, device=DEV),
+                     torch.zeros((37, 0), dtype=torch.uint8, device=DEV), 0, 0, None, None,
+                     synth.to_torch(bits, "bf16").to(DEV))
+    assert np.array_equal(np_bf16_bits(y), np.broadcast_to(bits, (5, 37)))
+
+
+def test_no_scale_means_one_and_f16_bias():
+    a = make_codes((96, 160), O.E4M3, 62, 0)
+    b = make_codes((80, 160), O.E4M3, 62, 1)
+    bv = synth.gaussian((80,), 30.0, "f16", 62, 2)
+    y = fp8mi.fp8_mm(to_dev_codes(a), to_dev_codes(b), 0, 0, None, None, torch.from_numpy(bv).to(DEV))
+    check(np_bf16_bits(y), a, O.E4M3, b, O.E4M3, 1.0, 1.0, bv.astype(np.float64))
+
+
+def test_strided_output_and_operands():
+    """Leading dimensions larger than the row: lda/ldb padded, output written
+    into a wider buffer whose padding stays untouched."""
+    M, N, K = 200, 150, 256
+    a = make_codes((M, K), O.E4M3, 63, 0)
+    b = make_codes((N, K), O.E4M3, 63, 1)
+    ab = torch.zeros((M, K + 64), dtype=torch.uint8, device=DEV)
+    bb = torch.zeros((N, K + 32), dtype=torch.uint8, device=DEV)
+    ab[:, :K] = to_dev_codes(a)
+    bb[:, :K] = to_dev_codes(b)
+    cb = torch.full((M, N + 7), 1234.0, dtype=torch.bfloat16, device=DEV)
+    fp8mi.fp8_mm(ab[:, :K], bb[:, :K], 0, 0, scalar(0.5), scalar(2.0), None, out=cb[:, :N])
+    check(np_bf16_bits(cb[:, :N]), a, O.E4M3, b, O.E4M3, 0.5, 2.0, None)
+    assert torch.all(cb[:, N:] == 1234.0)
+
+
+def test_identity_reproduces_operand():
+    """A = I (code 1.0 on the diagonal): C = bf16(B^T * sa * sb) exactly."""
+    K = 256
+    eye = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(eye, 0x38)
+    b = make_codes((192, K), O.E4M3, 64, 1)
+    y = fp8mi.fp8_mm(to_dev_codes(eye), to_dev_codes(b), 0, 0, scalar(0.25), scalar(4.0))
+    ref, _ = O.mm(eye, O.E4M3, b, O.E4M3, 0.25, 4.0)
+    assert np.array_equal(np_bf16_bits(y), ref[0])
+
+
+def test_repeat_determinism():
+    a = to_dev_codes(make_codes((1024, 1024), O.E4M3, 65, 0))
+    b = to_dev_codes(make_codes((1024, 1024), O.E4M3, 65, 1))
+    y0 = fp8mi.fp8_mm(a, b, 0, 0)
+    for _ in range(20):
+        assert torch.equal(fp8mi.fp8_mm(a, b, 0, 0), y0)
+
+
+# ----------------------------------------------------------------- exact data ----
+EXACT_CASES = [
+    # (M, N, K, batch, broadcast_b, fa, fb, bias)
+    (64, 256, 256, 1, False, O.E4M3, O.E4M3, True),          # tiny linear
+    (2048, 1536, 1536, 1, False, O.E4M3, O.E4M3, True),      # 1.2B-model linears
+    (2048, 6912, 1536, 1, False, O.E4M3, O.E4M3, True),
+    (2048, 1536, 6912, 1, False, O.E4M3, O.E4M3, True),
+    (4096, 4096, 4096, 1, False, O.E4M3, O.E4M3, True),      # square sweep
+    (8192, 8192, 8192, 1, False, O.E4M3, O.E4M3, False),
+    (64, 8192, 2048, 1, False, O.E4M3, O.E4M3, True),        # skinny
+    (1024, 1537, 2048, 1, False, O.E4M3, O.E4M3, True),      # odd N tail
+    (512, 512, 512, 64, True, O.E4M3, O.E4M3, True),         # bmm, stride-0 B
+    (1024, 2048, 2048, 8, False, O.E4M3, O.E4M3, False),
+    (8192, 1536, 6912, 1, False, O.E5M2, O.E4M3, False),     # training dX
+    (6912, 1536, 8192, 1, False, O.E5M2, O.E4M3, False),     # training dW
+    (77, 1000, 48, 1, False, O.E4M3, O.E5M2, True),          # ragged everything
+    (1, 1, 16, 3, False, O.E5M2, O.E5M2, True),
+]
+
+
+@pytest.mark.parametrize("case", EXACT_CASES, ids=lambda c: f"{c[3]}x{c[0]}x{c[1]}x{c[2]}-{c[5]}{c[6]}")
+def test_exact_integer_data(case):
+    M, N, K, batch, bcast, fa, fb, with_bias = case
+    key = M * 7 + N * 3 + K + batch
+    ashape = (batch, M, K) if batch > 1 else (M, K)
+    bshape = ((1 if bcast else batch), N, K) if batch > 1 else (N, K)
+    a = make_int_codes(ashape, fa, 70, key, 0)
+    b = make_int_codes(bshape, fb, 70, key, 1)
+    sa, sb = np.float32(2.0 ** -3), np.float32(2.0 ** 2)
+    bias_v = synth.rng(70, key, 2).integers(-4096, 4097, size=N).astype(np.float32) if with_bias else None
+    ad, bd = to_dev_codes(a), to_dev_codes(b)
+    if bcast:
+        bd = bd.expand(batch, N, K)
+    y = fp8mi.fp8_mm(ad, bd, FID[fa], FID[fb], scalar(sa), scalar(sb),
+                     torch.from_numpy(synth.f32_to_bf16_bits(bias_v).view(np.int16)).view(torch.bfloat16).to(DEV)
+                     if with_bias else None)
+    rows = sample_rows(M, 96, 70, key, 3)
+    bias = O.widen_to_f32(synth.f32_to_bf16_bits(bias_v), "bf16").astype(np.float64) if with_bias else None
+    check(np_bf16_bits(y), a, fa, b, fb, sa, sb, bias, rows, tag=f"exact {case}", exact=True)
