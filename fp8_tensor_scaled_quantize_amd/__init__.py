@@ -22,6 +22,12 @@ F32, F16, BF16 = 0, 1, 2
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+RING_SCRATCH_WORDS = 1024  # FP8MI_RING_SCRATCH_WORDS
+
+
+def ring_words_for(hist_len: int) -> int:
+    """FP8MI_RING_WORDS(hist_len)."""
+    return hist_len + 4 + RING_SCRATCH_WORDS
 
 
 class Fp8Error(RuntimeError):
@@ -59,8 +65,11 @@ def _ring_args(ring):
     if ring is None:
         return None, 0
     if ring.dim() != 1 or ring.dtype not in (torch.int32, torch.uint32) or not ring.is_contiguous():
-        raise ValueError("ring must be a contiguous 1-D int32 tensor of hist_len + 4 words")
-    return ring.data_ptr(), ring.numel() - 4
+        raise ValueError("ring must be a contiguous 1-D int32 tensor of hist_len + 4 + 1024 words")
+    h = ring.numel() - 4 - RING_SCRATCH_WORDS
+    if h < 1:
+        raise ValueError(f"ring of {ring.numel()} words is too short")
+    return ring.data_ptr(), h
 
 
 def version() -> str:
@@ -68,20 +77,21 @@ def version() -> str:
 
 
 def new_ring(hist_len: int, scale0: float = 1.0, device=None) -> torch.Tensor:
-    """A zeroed ring (history 0, slot 0, ticket 0, accumulator 0) holding
-    scale0 as its current scale: hist_len + 4 int32 words on `device`."""
-    w = torch.zeros(hist_len + 4, dtype=torch.int32)
+    """A zeroed ring (history 0, slot 0, ticket and scratch 0) holding scale0
+    as its current scale: FP8MI_RING_WORDS(hist_len) int32 words on `device`."""
+    w = torch.zeros(ring_words_for(hist_len), dtype=torch.int32)
     w[hist_len] = torch.tensor([scale0], dtype=torch.float32).view(torch.int32)[0]
     return w.to(device if device is not None else "cuda")
 
 
 def ring_words(ring: torch.Tensor):
-    """Host copy of a ring: dict of hist (fp32), scale, idx, ticket, acc."""
+    """Host copy of a ring: dict of hist (fp32), scale, idx, ticket and
+    whether the scratch region is all zero (as it is between calls)."""
     w = ring.detach().to("cpu")
-    h = w.numel() - 4
+    h = w.numel() - 4 - RING_SCRATCH_WORDS
     f = w.view(torch.float32)
     return {"hist": f[:h].clone(), "scale": float(f[h]), "idx": int(w[h + 1]),
-            "ticket": int(w[h + 2]), "acc": int(w[h + 3])}
+            "ticket": int(w[h + 2]), "scratch_clear": bool((w[h + 3:] == 0).all())}
 
 
 def fp8_quantize(x: torch.Tensor, fmt, transposed: bool = False, out: torch.Tensor | None = None,

@@ -135,49 +135,115 @@ template <int NT> __device__ __forceinline__ float block_max(float v, float* red
 }
 
 // ---------------------------------------------------------------------------
-// Ring fold: write amax into hist[slot], advance the slot modulo H, publish
-// fmt_max / max(hist) (1.0 when that maximum is 0 or not finite, or the
-// quotient is not a finite positive number).  Runs in one thread.
+// Ring fold, executed by one full wave (64 lanes): write amax into
+// hist[slot], advance the slot modulo H, publish fmt_max / max(hist) (1.0
+// when that maximum is 0 or not finite, or the quotient is not a finite
+// positive number).  The lanes read the history in parallel; the maximum of
+// the new window is max(amax, hist[i] for i != slot), which is exact in any
+// order.
 // ---------------------------------------------------------------------------
-template <int FMT> __device__ void ring_fold(uint32_t* ring, int H, float amax) {
-  float* hist = reinterpret_cast<float*>(ring);
-  uint32_t slot = ring[H + 1] % (uint32_t)H;
-  hist[slot] = amax;
-  slot = (slot + 1u == (uint32_t)H) ? 0u : slot + 1u;
-  float m = hist[0];
-  for (int i = 1; i < H; ++i) m = fmaxf(m, hist[i]);
-  float s = 1.0f;
-  if (m > 0.0f && m <= 3.40282347e38f) {
-    const float q = FmtTraits<FMT>::kMax / m;  // IEEE division
-    if (q > 0.0f && q <= 3.40282347e38f) s = q;
+template <int FMT>
+__device__ void ring_fold_wave(uint32_t* ring, int H, float amax, float* scale_inv_out, float s_used,
+                               float* amax_out) {
+  const int lane = threadIdx.x & 63;
+  const float* hist = reinterpret_cast<const float*>(ring);
+  const uint32_t slot = ring[H + 1] % (uint32_t)H;
+  float m = amax;
+  for (int i = lane; i < H; i += 64)
+    if ((uint32_t)i != slot) m = fmaxf(m, hist[i]);
+  m = wave_max(m);
+  if (lane == 0) {
+    float s = 1.0f;
+    if (m > 0.0f && m <= 3.40282347e38f) {
+      const float q = FmtTraits<FMT>::kMax / m;  // IEEE division
+      if (q > 0.0f && q <= 3.40282347e38f) s = q;
+    }
+    reinterpret_cast<float*>(ring)[slot] = amax;
+    ring[H] = __float_as_uint(s);
+    ring[H + 1] = (slot + 1u == (uint32_t)H) ? 0u : slot + 1u;
+    if (scale_inv_out) *scale_inv_out = 1.0f / s_used;
+    if (amax_out) *amax_out = amax;
   }
-  ring[H] = __float_as_uint(s);
-  ring[H + 1] = slot;
 }
 
-// End of a ring-mode quantize workgroup: publish this block's amax into the
-// ring's accumulator and take a ticket; the block that takes the last ticket
-// folds the accumulated amax into the ring, writes the outputs that belong to
-// the whole call and re-arms ticket and accumulator.  Thread 0 only.
+// ---------------------------------------------------------------------------
+// Cross-workgroup amax publication.
 //
-// Ordering: the amax max and the ticket are device-scope atomics; the ticket
-// add is acq_rel, so every block's accumulator update happens-before the last
-// block's read of it, across all XCDs.
+// Device-scope atomics to one address serialise across the XCDs (about 12 ns
+// each on MI355X), so workgroups spread their partial amax over kFoldSlots
+// slots on separate 128-byte lines of the ring's scratch region: a workgroup
+// maxes its amax into slot (id % nslot) and takes that slot's ticket; the
+// last member of each slot takes the completion ticket; the workgroup that
+// takes the last completion ticket reduces the slots, folds, and clears the
+// scratch.  Ordering rests on returning device-scope atomics: every atomic
+// below returns its old value, and a workgroup waits for each to come back
+// (s_waitcnt vmcnt(0)) before issuing the next, so its partial amax is
+// performed at the device's coherence point before its ticket is; the slot
+// and completion tickets are totally ordered per address, and the final
+// reads are device-scope atomic loads.  No L2 write-back fence is needed
+// because no plain store is read by another workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kFoldSlots = 32;
+constexpr int kFoldSlotStride = 32;  // words: 128 bytes between slots
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t dev_load(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t dev_max(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t dev_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t dev_xchg(uint32_t* p, uint32_t v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Max a non-negative fp32 into a word holding fp32 bits; skips the
+// read-modify-write when the word already holds at least as much.
+__device__ __forceinline__ void publish_max(uint32_t* p, float v) {
+  const uint32_t bits = __float_as_uint(v);
+  if (bits > dev_load(p)) {
+    const uint32_t old = dev_max(p, bits);
+    asm volatile("" ::"v"(old));  // keep the returning form of the atomic
+  }
+  wait_vmem();
+}
+
+// End of a ring-mode quantize workgroup; every thread of the block calls it
+// with the block's amax.  `flag` is one word of LDS.
 template <int FMT>
-__device__ void ring_block_done(uint32_t* ring, int H, float block_amax, float s_used,
-                                float* scale_inv_out, float* amax_out) {
-  uint32_t* ticket = ring + H + 2;
-  uint32_t* acc = ring + H + 3;
-  __hip_atomic_fetch_max(acc, __float_as_uint(block_amax), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ void ring_block_done(uint32_t* ring, int H, float block_amax, float s_used, float* scale_inv_out,
+                                float* amax_out, uint32_t* flag) {
   const uint32_t nblk = gridDim.x * gridDim.y * gridDim.z;
-  const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  if (t != nblk - 1u) return;
-  const float a = __uint_as_float(__hip_atomic_load(acc, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
-  if (scale_inv_out) *scale_inv_out = 1.0f / s_used;
-  if (amax_out) *amax_out = a;
-  ring_fold<FMT>(ring, H, a);
-  __hip_atomic_store(acc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(ticket, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t nslot = nblk < (uint32_t)kFoldSlots ? nblk : (uint32_t)kFoldSlots;
+  uint32_t* scratch = ring + H + 4;
+  if (threadIdx.x == 0) {
+    const uint32_t bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t slot = bid % nslot;
+    uint32_t* sl = scratch + slot * kFoldSlotStride;
+    const uint32_t old = dev_max(sl, __float_as_uint(block_amax));
+    asm volatile("" ::"v"(old));  // keep the returning form of the atomic
+    wait_vmem();
+    const uint32_t members = nblk / nslot + (slot < nblk % nslot ? 1u : 0u);
+    bool last = dev_add(sl + 1, 1u) == members - 1u;
+    if (last) last = dev_add(ring + H + 2, 1u) == nslot - 1u;
+    *flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*flag == 0u || threadIdx.x >= 64) return;
+  // The last workgroup: wave 0 reduces the slots, folds, clears the scratch.
+  const int lane = threadIdx.x;
+  float a = (uint32_t)lane < nslot ? __uint_as_float(dev_load(scratch + lane * kFoldSlotStride)) : 0.0f;
+  a = wave_max(a);
+  ring_fold_wave<FMT>(ring, H, a, scale_inv_out, s_used, amax_out);
+  if ((uint32_t)lane < nslot) {
+    (void)dev_xchg(scratch + lane * kFoldSlotStride, 0u);
+    (void)dev_xchg(scratch + lane * kFoldSlotStride + 1, 0u);
+  }
+  if (lane == 0) (void)dev_xchg(ring + H + 2, 0u);
 }
 
 }  // namespace fp8mi

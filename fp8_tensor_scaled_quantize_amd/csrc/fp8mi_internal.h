@@ -26,6 +26,10 @@ struct MmArgs {
   int bias_dtype;  // -1: no bias
   uint16_t* c;
   int64_t ldc, stride_c;
+
+  // Bytes of one batch's A (B) from row r on: the last row ends at K.
+  __host__ __device__ int64_t a_extent_from(int64_t r) const { return r < M ? (M - 1 - r) * lda + K : 0; }
+  __host__ __device__ int64_t b_extent_from(int64_t r) const { return r < N ? (N - 1 - r) * ldb + K : 0; }
 };
 
 hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);

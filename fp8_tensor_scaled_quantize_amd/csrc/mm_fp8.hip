@@ -15,7 +15,7 @@
 // The operands are swapped at the MFMA (B rows drive the instruction's first
 // operand), so each lane ends with 4 consecutive output columns of one row
 // and writes 8 contiguous bytes of bf16.  LDS tiles hold 128 K-bytes per row,
-// 16-byte chunks XOR-swizzled by (row & 7) so that the 16 rows one MFMA
+// 16-byte chunks XOR-swizzled (see swz) so that the 16 rows one MFMA
 // fragment reads spread over the banks.
 #include "fp8mi_device.h"
 #include "fp8mi_internal.h"
@@ -28,8 +28,18 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kBK = 128;
 constexpr int kMmThreads = 256;
 
+// LDS tiles: rows of kBK = 128 bytes; the 16-byte chunk c of row r sits at
+// chunk position c ^ swz(r).  gfx950 serves a ds_read_b128 16 lanes per cycle
+// from 64 four-byte banks, each half-wave in two cycles split by the parity
+// of lane bits 2..4 (measured with the LDS bank-conflict counter).  In an
+// MFMA fragment read lane l reads row l%16, chunk 2(l/16) + h; swz(r) =
+// ((r >> 1) & 1) | (r & 4) puts every such cycle's 16 reads on 16 distinct
+// 16-byte bank groups (row parity picks the 128-byte half, the chunk
+// position the group within it).
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 1) | (row & 4); }
+
 __device__ __forceinline__ v8i lds_frag(const uint8_t* S, int row, int g) {
-  const int sw = row & 7;
+  const int sw = swz(row);
   const uint4 lo = *reinterpret_cast<const uint4*>(S + row * kBK + (((2 * g) ^ sw) << 4));
   const uint4 hi = *reinterpret_cast<const uint4*>(S + row * kBK + (((2 * g + 1) ^ sw) << 4));
   v8i r;
@@ -86,12 +96,12 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int id = tid + kMmThreads * i, row = id >> 3, ch = id & 7;
-      *reinterpret_cast<uint4*>(As + row * kBK + ((ch ^ (row & 7)) << 4)) = ra[i];
+      *reinterpret_cast<uint4*>(As + row * kBK + ((ch ^ swz(row)) << 4)) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int id = tid + kMmThreads * i, row = id >> 3, ch = id & 7;
-      *reinterpret_cast<uint4*>(Bs + row * kBK + ((ch ^ (row & 7)) << 4)) = rb[i];
+      *reinterpret_cast<uint4*>(Bs + row * kBK + ((ch ^ swz(row)) << 4)) = rb[i];
     }
   };
 
@@ -158,7 +168,189 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
   }
 }
 
+// ===========================================================================
+// Large-tile kernel: 256 x 256 block tile, 8 waves (2 along M x 4 along N),
+// each wave 128 x 64 = 8 x 4 MFMA tiles (128 fp32 accumulators per lane).
+// K advances 128 bytes per step through two LDS stages (2 x 64 KiB).  The
+// operands go from HBM/L2 straight into LDS (buffer_load_dwordx4 ... lds):
+// each load instruction fills 1 KiB = 8 tile rows, lane l writing 16 bytes at
+// l * 16, so lane l fetches the 16-byte chunk that the XOR swizzle places
+// there (row r0 + l/8, chunk (l%8) ^ (l/8)).  The loads of step k+1 are in
+// flight while step k's MFMAs run; one wait + barrier per step.  Rows past
+// the matrix edge and chunks past K read as zero: their buffer offsets lie
+// beyond the resource's byte count.
+// Workgroups are renumbered so that the ones a single XCD runs (the hardware
+// deals workgroup ids round-robin over the 8 XCDs) cover a compact block of
+// tiles -- group_m tile rows by consecutive tile columns -- and share their
+// A and B panels in that XCD's L2.
+// ===========================================================================
+constexpr int kBigThreads = 512;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, dword3 as for
+// all gfx9 raw buffers); reads at offsets >= bytes return zero.
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xFFFF);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS at lds + 16 * lane.
+// Written as asm so that the compiler's wait-count pass does not treat the
+// LDS write as aliasing the current stage's ds_reads (it would otherwise wait
+// for this prefetch before every read); the kernel waits for it explicitly
+// (s_waitcnt vmcnt(0) + barrier) before the stage is read.  The asm has no
+// register outputs; M0 is saved and restored around it.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+__device__ __forceinline__ void tile_coords(int64_t wg, int64_t tiles_m, int64_t tiles_n, int group_m,
+                                            int64_t& tm, int64_t& tn) {
+  const int64_t T = tiles_m * tiles_n;
+  const int64_t full = (T / 8) * 8;
+  int64_t id = wg;
+  if (wg < full) id = (wg % 8) * (full / 8) + wg / 8;  // same-XCD workgroups get consecutive ids
+  const int64_t per_group = (int64_t)group_m * tiles_n;
+  const int64_t g = id / per_group, r = id % per_group;
+  const int64_t rows_here = (tiles_m - g * group_m) < group_m ? (tiles_m - g * group_m) : group_m;
+  tm = g * group_m + r % rows_here;
+  tn = r / rows_here;
+}
+
+template <int FA, int FB>
+__global__ void __launch_bounds__(kBigThreads, 1) mm_fp8_256(MmArgs p, int64_t tiles_m, int64_t tiles_n,
+                                                             int group_m) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int WM = 128, WN = 64;
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int STAGE = (BM + BN) * kBK;      // bytes per LDS stage
+  constexpr int LOADS = BM / 8 / 8;           // load instructions per wave per operand (4)
+  __shared__ __align__(16) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 2, wn = wid & 3;
+  const int64_t bz = blockIdx.z;
+  int64_t tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int ext_a = (int)p.a_extent_from(m0), ext_b = (int)p.b_extent_from(n0);
+  const v4i rsa = buffer_rsrc(p.a + bz * p.stride_a + m0 * p.lda, ext_a);
+  const v4i rsb = buffer_rsrc(p.b + bz * p.stride_b + n0 * p.ldb, ext_b);
+  // Lane l of a 1 KiB load fills LDS row r0 + l/8 (r0 a multiple of 8) at
+  // chunk position l%8, so it fetches logical chunk (l%8) ^ swz(l/8).
+  const int lr = lane >> 3, lc = (lane & 7) ^ swz(lr);
+  const int lda = (int)p.lda, ldb = (int)p.ldb;
+  const int va = lr * lda + 16 * lc, vb = lr * ldb + 16 * lc;
+  const int K = (int)p.K;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+
+  // Issue one stage of loads (this wave's 4 + 4 instructions).
+  auto issue = [&](int stage, int k0) {
+    const bool past = k0 + 16 * lc >= K;  // K tail: chunks at or past K read as zero
+    const int oa = past ? ext_a : va, ob = past ? ext_b : vb;
+    const uint32_t as = smem_lds + stage * STAGE, bs = as + BM * kBK;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r0 = (wid * LOADS + i) * 8;
+      dma16(rsa, as + r0 * kBK, oa, k0 + r0 * lda);
+      dma16(rsb, bs + r0 * kBK, ob, k0 + r0 * ldb);
+    }
+  };
+
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nk = (K + kBK - 1) / kBK;
+  const int r16 = lane & 15, g = lane >> 4;
+  if (nk > 0) issue(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kBK);
+    const uint8_t* As = smem + (kt & 1) * STAGE;
+    const uint8_t* Bs = As + BM * kBK;
+    v8i bfr[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) bfr[j] = lds_frag(Bs, wn * WN + 16 * j + r16, g);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const v8i af = lds_frag(As, wm * WM + 16 * i + r16, g);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_nt<FA, FB>(bfr[j], af, acc[i][j]);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // Epilogue: y = acc * fl32(sa * sb) + bias[j], one bf16 rounding.
+  const float sa = p.a_scale_inv ? *p.a_scale_inv : 1.0f;
+  const float sb = p.b_scale_inv ? *p.b_scale_inv : 1.0f;
+  const float sab = sa * sb;
+  uint16_t* C = p.c + bz * p.stride_c;
+  const int ng = lane >> 4;
+  float bias_v[TJ][4];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng + r;
+      bias_v[j][r] = (p.bias && gn < p.N) ? load_bias(p.bias, p.bias_dtype, gn) : 0.0f;
+    }
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int64_t gm = m0 + wm * WM + 16 * i + r16;
+    if (gm >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng;
+      if (gn >= p.N) continue;
+      uint32_t h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bias_v[j][r]));
+      uint16_t* dst = C + gm * p.ldc + gn;
+      if (gn + 4 <= p.N && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (gn + r < p.N) dst[r] = (uint16_t)h[r];
+      }
+    }
+  }
+}
+
+// Tile dispatch: the 256 x 256 kernel when the problem fills the machine
+// with it (batch x tiles >= CU count); the 128 x 128 kernel otherwise.
 template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStream_t st) {
+  const int ncu = device_cu_count();
+  const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  // buffer offsets are 32-bit: extent + largest soffset must stay below 2^32
+  const bool fits31 = p.a_extent_from(0) < (1ll << 31) && p.b_extent_from(0) < (1ll << 31) && p.K < (1ll << 30);
+  if (t256 * p.batch >= ncu && fits31) {
+    const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    const int group_m = 4;
+    const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
+    hipLaunchKernelGGL((mm_fp8_256<FA, FB>), grid, dim3(kBigThreads), 0, st, p, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+  }
   constexpr int BM = 128, BN = 128;
   const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.batch);
   hipLaunchKernelGGL((mm_fp8_tile<BM, BN, FA, FB>), grid, dim3(kMmThreads), 0, st, p);

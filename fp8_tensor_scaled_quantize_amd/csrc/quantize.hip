@@ -44,13 +44,10 @@ struct QuantArgs {
 template <int FMT, int NT>
 __device__ __forceinline__ void quant_block_done(const QuantArgs& p, float thread_amax, float s, float* red) {
   const float bmax = block_max<NT>(thread_amax, red);
-  if (threadIdx.x != 0) return;
   if (p.ring) {
-    ring_block_done<FMT>(p.ring, p.H, bmax, s, p.scale_inv_out, p.amax_out);
-  } else {
-    if (p.amax_out)
-      __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(p.amax_out), __float_as_uint(bmax), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+    ring_block_done<FMT>(p.ring, p.H, bmax, s, p.scale_inv_out, p.amax_out, reinterpret_cast<uint32_t*>(red));
+  } else if (threadIdx.x == 0) {
+    if (p.amax_out) publish_max(reinterpret_cast<uint32_t*>(p.amax_out), bmax);
     if (p.scale_inv_out && blockIdx.x == 0 && blockIdx.y == 0) *p.scale_inv_out = 1.0f / s;
   }
 }
@@ -79,7 +76,52 @@ constexpr int kFlatThreads = 256;
 constexpr int kFlatElemsPerThread = 16;
 constexpr int kFlatWaveStep = 64 * kFlatElemsPerThread;                   // 1024 elements
 constexpr int kFlatBlockStep = kFlatThreads * kFlatElemsPerThread;      // 4096 elements
+constexpr int kFlatUnroll = 2;                                          // block steps in flight per lane
 
+// Encode one lane's 16 elements of a wave step (already loaded) and store the codes.
+template <int DT, int FMT, int NL, int EPL>
+__device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t* out_w0, int lane, float s) {
+  float f[kFlatElemsPerThread];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    if constexpr (DT == kF32) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[j * 4 + e] = __uint_as_float(w[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) widen2<DT>(w[e], f[j * 8 + 2 * e], f[j * 8 + 2 * e + 1]);
+    }
+  }
+  bool nan = false;
+  float camax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kFlatElemsPerThread; ++e) {
+    camax = fmaxf(camax, fabsf(f[e]));
+    nan |= f[e] != f[e];
+  }
+  if (nan) camax = nan_free_absmax<kFlatElemsPerThread>(f);
+  uint32_t code[kFlatElemsPerThread / 4];
+  if (!nan) {
+#pragma unroll
+    for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
+      code[q] = cvt4<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
+  } else {
+#pragma unroll
+    for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
+      code[q] = enc4_exact<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
+  }
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    uint8_t* o = out_w0 + (int64_t)(j * 64 + lane) * EPL;
+    if constexpr (EPL == 8) *reinterpret_cast<uint2*>(o) = make_uint2(code[2 * j], code[2 * j + 1]);
+    else *reinterpret_cast<uint32_t*>(o) = code[j];
+  }
+  return camax;
+}
+
+// Each block handles `steps_per_block` consecutive block steps, kFlatUnroll at
+// a time with all of their loads issued before any is consumed.
 template <int DT, int FMT>
 __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64_t n, int64_t steps_per_block) {
   __shared__ float red[kFlatThreads / 64];
@@ -93,51 +135,31 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
   const int64_t first = (int64_t)blockIdx.x * steps_per_block;
   const int64_t total_steps = (n + kFlatBlockStep - 1) / kFlatBlockStep;
   const int64_t last = first + steps_per_block < total_steps ? first + steps_per_block : total_steps;
-  for (int64_t st = first; st < last; ++st) {
+  int64_t st = first;
+  // full unrolled groups: every wave step of the group lies inside the tensor
+  for (; st + kFlatUnroll <= last && (st + kFlatUnroll) * kFlatBlockStep <= n; st += kFlatUnroll) {
+    uint4 v[kFlatUnroll][NL];
+#pragma unroll
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      const int64_t w0 = (st + u) * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        v[u][j] = *reinterpret_cast<const uint4*>(xb + (w0 + (int64_t)(j * 64 + lane) * EPL) * EB);
+    }
+#pragma unroll
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      const int64_t w0 = (st + u) * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
+      amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v[u], p.out_row + w0, lane, s));
+    }
+  }
+  for (; st < last; ++st) {
     const int64_t w0 = st * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
     if (w0 + kFlatWaveStep <= n) {
       uint4 v[NL];
 #pragma unroll
       for (int j = 0; j < NL; ++j)
         v[j] = *reinterpret_cast<const uint4*>(xb + (w0 + (int64_t)(j * 64 + lane) * EPL) * EB);
-      float f[kFlatElemsPerThread];
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        if constexpr (DT == kF32) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[j * 4 + e] = __uint_as_float(w[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) widen2<DT>(w[e], f[j * 8 + 2 * e], f[j * 8 + 2 * e + 1]);
-        }
-      }
-      bool nan = false;
-      float camax = 0.0f;
-#pragma unroll
-      for (int e = 0; e < kFlatElemsPerThread; ++e) {
-        camax = fmaxf(camax, fabsf(f[e]));
-        nan |= f[e] != f[e];
-      }
-      if (nan) camax = nan_free_absmax<kFlatElemsPerThread>(f);
-      amax = fmaxf(amax, camax);
-      uint32_t code[kFlatElemsPerThread / 4];
-      if (!nan) {
-#pragma unroll
-        for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
-          code[q] = cvt4<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
-      } else {
-#pragma unroll
-        for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
-          code[q] = enc4_exact<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
-      }
-      // store: load j's EPL codes go to out[w0 + (j*64+lane)*EPL ...]
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        uint8_t* o = p.out_row + w0 + (int64_t)(j * 64 + lane) * EPL;
-        if constexpr (EPL == 8) *reinterpret_cast<uint2*>(o) = make_uint2(code[2 * j], code[2 * j + 1]);
-        else *reinterpret_cast<uint32_t*>(o) = code[j];
-      }
+      amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v, p.out_row + w0, lane, s));
     } else if (w0 < n) {
       // ragged end of the tensor: element by element, same lane mapping
 #pragma unroll
@@ -290,7 +312,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
 
 // Fold alone / arming of a ring-less amax output.
 template <int FMT> __global__ void amax_fold_kernel(uint32_t* ring, int H, const float* amax) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) ring_fold<FMT>(ring, H, *amax);
+  if (threadIdx.x < 64) ring_fold_wave<FMT>(ring, H, *amax, nullptr, 1.0f, nullptr);
 }
 __global__ void zero_word_kernel(float* p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0.0f;
@@ -301,6 +323,11 @@ __global__ void zero_word_kernel(float* p) {
 // ===========================================================================
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Persistent grids: at most this many workgroups per CU; each loops over an
+// equal share of the work (fewer workgroups -> fewer cross-XCD atomics).
+constexpr int kFlatBlocksPerCU = 8;
+constexpr int kTileBlocksPerCU = 8;
+
 template <int DT, int FMT>
 static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int ncu = device_cu_count();
@@ -310,7 +337,7 @@ static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
                               (reinterpret_cast<uintptr_t>(p.out_row) & 15u) == 0;
   if (contiguous_row || n == 0) {
     const int64_t steps = cdiv(n, kFlatBlockStep);
-    const int64_t max_blocks = (int64_t)ncu * 8;
+    const int64_t max_blocks = (int64_t)ncu * kFlatBlocksPerCU;
     const int64_t spb = steps <= max_blocks ? 1 : cdiv(steps, max_blocks);
     const int64_t blocks = steps == 0 ? 1 : cdiv(steps, spb);
     hipLaunchKernelGGL((quantize_flat<DT, FMT>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n, spb);
@@ -318,7 +345,7 @@ static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   }
   const int64_t tiles_c = cdiv(p.cols, kTileC);
   const int64_t ntiles = cdiv(p.rows, kTileR) * tiles_c;
-  const int64_t max_blocks = (int64_t)ncu * 8;
+  const int64_t max_blocks = (int64_t)ncu * kTileBlocksPerCU;
   const int64_t tpb = ntiles <= max_blocks ? 1 : cdiv(ntiles, max_blocks);
   const int64_t blocks = cdiv(ntiles, tpb);
   switch (mode) {

@@ -27,19 +27,22 @@
  *
  * Ring (delayed scaling; log:tests/extension, the commits that pack
  * [history | scale | counter] into one device buffer and fold it in the
- * quantize kernel's last block).  A ring is H + 4 32-bit device words:
- *   [0, H)  amax history, fp32
- *   H       current scale, fp32 (the scale the next quantize call uses)
- *   H+1     next history slot, uint32 in [0, H)
- *   H+2     completion ticket, uint32, 0 at rest
- *   H+3     amax accumulator (fp32 bits as uint32), 0 at rest
- * The caller initialises it (history 0, slot 0, ticket 0, accumulator 0,
- * scale = a starting scale) and may copy it to checkpoint / restore.  A fold
- * of amax a writes a into hist[slot], advances slot modulo H, and publishes
+ * quantize kernel's last block).  A ring for a history of H amaxes is
+ * FP8MI_RING_WORDS(H) = H + 4 + 1024 32-bit device words:
+ *   [0, H)        amax history, fp32
+ *   H             current scale, fp32 (the scale the next quantize call uses)
+ *   H+1           next history slot, uint32 in [0, H)
+ *   H+2           completion ticket, uint32, 0 at rest
+ *   H+3           reserved, 0
+ *   [H+4, H+1028) fold scratch: per-slot partial amax and counters on 32
+ *                 separate 128-byte lines, all 0 at rest
+ * The caller initialises it (history 0, slot 0, scale = a starting scale,
+ * every other word 0) and may copy it to checkpoint / restore.  A fold of
+ * amax a writes a into hist[slot], advances slot modulo H, and publishes
  * scale = fmt_max / max(hist) -- or 1.0 when that maximum is 0 or not finite
  * or the quotient is not a finite positive number.  After every call the
- * ticket and accumulator are 0 again.  One ring may be used by at most one
- * call in flight at a time.
+ * ticket and the scratch words are 0 again.  One ring may be used by at most
+ * one call in flight at a time.
  */
 #ifndef FP8MI_H
 #define FP8MI_H
@@ -70,8 +73,10 @@ typedef enum {
 typedef enum { FP8MI_E4M3 = 0, FP8MI_E5M2 = 1 } fp8mi_format;
 typedef enum { FP8MI_F32 = 0, FP8MI_F16 = 1, FP8MI_BF16 = 2 } fp8mi_dtype;
 
-/* Largest history window a ring may have. */
+/* Largest history window a ring may have, and the ring size in words. */
 #define FP8MI_MAX_HIST 4096
+#define FP8MI_RING_SCRATCH_WORDS 1024
+#define FP8MI_RING_WORDS(H) ((H) + 4 + FP8MI_RING_SCRATCH_WORDS)
 
 /*
  * fp8_quantize -- per-tensor scaled cast of a [rows, cols] tensor to fp8 in
@@ -87,7 +92,7 @@ typedef enum { FP8MI_F32 = 0, FP8MI_F16 = 1, FP8MI_BF16 = 2 } fp8mi_dtype;
  *              1: out[j * ld_out + i] = q(i, j), ld_out >= rows.
  *              Bytes of `out` outside the rows x cols codes are not written.
  *   scale      device fp32 per-tensor scale, or NULL;
- *   ring       device ring of hist_len + 4 words, or NULL.  Exactly one of
+ *   ring       device ring of FP8MI_RING_WORDS(hist_len) words, or NULL.  Exactly one of
  *              scale / ring is given (else FP8MI_ERR_ARG).  With a ring the
  *              call uses the ring's current scale and its last workgroup folds
  *              this call's amax into the ring (the next scale is published
@@ -120,7 +125,8 @@ FP8MI_API fp8mi_status fp8_quantize_dual(const void* x, int x_dtype, int64_t row
  * (e.g. one reduced over several devices): one tiny launch that performs
  * exactly the fold a ring-mode quantize performs in its last workgroup
  * (log:tests/extension, the commit testing the in-kernel fold against a host
- * reference).  ring: device, hist_len + 4 words; amax: device fp32.
+ * reference).  ring: device, FP8MI_RING_WORDS(hist_len) words; amax:
+ * device fp32.
  */
 FP8MI_API fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const float* amax, int fmt, void* stream);
 

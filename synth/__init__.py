@@ -62,3 +62,12 @@ def to_torch(x: np.ndarray, dtype: str):
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(x))
+
+
+def device_gaussian(shape, sigma: float, dtype, seed: int, device="cuda"):
+    """N(0, sigma^2) drawn on the device with a seeded torch generator (for
+    large benchmark inputs where host generation would dominate)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * sigma).to(dtype)

@@ -68,9 +68,21 @@ def as_bits(v) -> int:
     return int(np.array([v], np.float32).view(np.uint32)[0])
 
 
+RING_SCRATCH = 1024
+
+
+def ring_state_words(ring: torch.Tensor) -> np.ndarray:
+    """The H + 4 state words of a device ring (history, scale, slot, ticket,
+    reserved) after checking that its scratch region is clear."""
+    w = ring.cpu().numpy().view(np.uint32)
+    assert not w[-RING_SCRATCH:].any(), "ring scratch not cleared after the call"
+    return w[:-RING_SCRATCH]
+
+
 def ring_to_oracle(ring: torch.Tensor) -> "O.Ring":
-    return O.Ring.from_words(ring.cpu().numpy().view(np.uint32))
+    return O.Ring.from_words(ring_state_words(ring))
 
 
 def ring_from_oracle(r: "O.Ring") -> torch.Tensor:
-    return torch.from_numpy(r.words().view(np.int32).copy()).to(DEV)
+    w = np.concatenate([r.words(), np.zeros(RING_SCRATCH, np.uint32)])
+    return torch.from_numpy(w.view(np.int32).copy()).to(DEV)
