@@ -14,7 +14,7 @@ import torch
 from ._lib import lib
 
 __all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual",
-           "fp8_amax_fold", "fp8_mm", "new_ring", "ring_words", "version"]
+           "fp8_amax_fold", "fp8_mm", "fp8_bias_grad", "fp8_ring_seed", "new_ring", "ring_words", "version"]
 
 E4M3, E5M2 = 0, 1
 F32, F16, BF16 = 0, 1, 2
@@ -176,3 +176,25 @@ def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_inv
     _check(lib().fp8_mm(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
                         _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(out), ldc, sc, _stream(a)))
     return out
+
+
+def fp8_bias_grad(dy: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Bias gradient: sum of a bf16/fp16 gradient over every leading
+    dimension (fp64 accumulation, one bf16 rounding) -> bf16 [cols]."""
+    if dy.dim() < 1 or (dy.shape[-1] > 1 and dy.stride(-1) != 1):
+        raise ValueError("dy needs unit stride along its last dimension")
+    cols = dy.shape[-1]
+    d2 = dy.reshape(-1, cols)
+    rows = d2.shape[0]
+    ld = d2.stride(0) if rows > 1 else cols
+    if out is None:
+        out = torch.empty(cols, dtype=torch.bfloat16, device=dy.device)
+    _check(lib().fp8_bias_grad(_ptr(d2), _DT[dy.dtype], rows, cols, ld, _ptr(out), _stream(dy)))
+    return out
+
+
+def fp8_ring_seed(ring: torch.Tensor, amax: torch.Tensor, fmt) -> None:
+    """Reset a ring and publish the scale a fold of `amax` into an empty
+    window gives (fmt_max / amax, or 1.0)."""
+    rp, h = _ring_args(ring)
+    _check(lib().fp8_ring_seed(rp, h, _ptr(amax), _fmt(fmt), _stream(ring)))

@@ -168,6 +168,33 @@ fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, 
   return from_hip(launch_mm(p, fmt_a, fmt_b, static_cast<hipStream_t>(stream)), "mm launch");
 }
 
+fp8mi_status fp8_bias_grad(const void* dy, int dy_dtype, int64_t rows, int64_t cols, int64_t ld, void* out,
+                           void* stream) {
+  if (!valid_dtype(dy_dtype)) return fail(FP8MI_ERR_ENUM, "dy_dtype %d is not F32/F16/BF16", dy_dtype);
+  if (dy_dtype == FP8MI_F32) return fail(FP8MI_ERR_UNSUPPORTED, "fp8_bias_grad takes bf16 or fp16 gradients");
+  if (rows < 0 || cols < 0) return fail(FP8MI_ERR_SHAPE, "negative shape rows=%lld cols=%lld", (long long)rows,
+                                        (long long)cols);
+  if (cols == 0) return FP8MI_OK;
+  if (!out) return fail(FP8MI_ERR_NULL, "out is NULL");
+  if (rows > 0 && !dy) return fail(FP8MI_ERR_NULL, "dy is NULL");
+  if (rows > 0 && ld < cols) return fail(FP8MI_ERR_SHAPE, "ld %lld < cols %lld", (long long)ld, (long long)cols);
+  if ((reinterpret_cast<uintptr_t>(dy) & 1u) || (reinterpret_cast<uintptr_t>(out) & 1u))
+    return fail(FP8MI_ERR_ARG, "dy and out must be 2-byte aligned");
+  if ((cols + 63) / 64 > 0x7FFFFFFF) return fail(FP8MI_ERR_UNSUPPORTED, "cols beyond the launch grid");
+  return from_hip(launch_grad_bias(dy, dy_dtype, rows, cols, ld, static_cast<uint16_t*>(out),
+                                   static_cast<hipStream_t>(stream)),
+                  "bias grad launch");
+}
+
+fp8mi_status fp8_ring_seed(uint32_t* ring, int32_t hist_len, const float* amax, int fmt, void* stream) {
+  if (!ring) return fail(FP8MI_ERR_NULL, "ring is NULL");
+  if (!amax) return fail(FP8MI_ERR_NULL, "amax is NULL");
+  if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
+  fp8mi_status s = check_scale_ring(nullptr, ring, hist_len);
+  if (s != FP8MI_OK) return s;
+  return from_hip(launch_ring_seed(ring, hist_len, amax, fmt, static_cast<hipStream_t>(stream)), "seed launch");
+}
+
 const char* fp8mi_status_string(int s) {
   switch (s) {
     case FP8MI_OK: return "ok";

@@ -185,6 +185,7 @@ __device__ void ring_fold_wave(uint32_t* ring, int H, float amax, float* scale_i
 // ---------------------------------------------------------------------------
 constexpr int kFoldSlots = 32;
 constexpr int kFoldSlotStride = 32;  // words: 128 bytes between slots
+static_assert(kFoldSlots * kFoldSlotStride == 1024, "ring scratch is FP8MI_RING_SCRATCH_WORDS words");
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -231,19 +231,22 @@ __device__ __forceinline__ void tile_coords(int64_t wg, int64_t tiles_m, int64_t
   tn = r / rows_here;
 }
 
-template <int FA, int FB>
-__global__ void __launch_bounds__(kBigThreads, 1) mm_fp8_256(MmArgs p, int64_t tiles_m, int64_t tiles_n,
-                                                             int group_m) {
+template <int FA, int FB, int WAVES_M, int WAVES_N>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) mm_fp8_256(MmArgs p, int64_t tiles_m, int64_t tiles_n,
+                                                                        int group_m) {
   constexpr int BM = 256, BN = 256;
-  constexpr int WM = 128, WN = 64;
+  constexpr int NWAVES = WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TI = WM / 16, TJ = WN / 16;
   constexpr int STAGE = (BM + BN) * kBK;      // bytes per LDS stage
-  constexpr int LOADS = BM / 8 / 8;           // load instructions per wave per operand (4)
-  __shared__ __align__(16) uint8_t smem[2 * STAGE];
+  constexpr int LOADS = BM / 8 / NWAVES;      // 1 KiB load instructions per wave per operand
+  constexpr int CROW = BN + 8;                // bf16 per LDS row of the staged C tile (16 B pad)
+  constexpr int SMEM = 2 * STAGE > BM * CROW * 2 ? 2 * STAGE : BM * CROW * 2;
+  __shared__ __align__(16) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 2, wn = wid & 3;
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int64_t bz = blockIdx.z;
   int64_t tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -260,16 +263,18 @@ __global__ void __launch_bounds__(kBigThreads, 1) mm_fp8_256(MmArgs p, int64_t t
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
 
   // Issue one stage of loads (this wave's 4 + 4 instructions).
-  auto issue = [&](int stage, int k0) {
+  // Load instruction q (0 .. 2*LOADS-1) of one stage: even q -> A, odd q -> B,
+  // rows (wid * LOADS + q / 2) * 8 .. + 7.
+  auto issue_one = [&](int stage, int k0, int q) {
     const bool past = k0 + 16 * lc >= K;  // K tail: chunks at or past K read as zero
-    const int oa = past ? ext_a : va, ob = past ? ext_b : vb;
     const uint32_t as = smem_lds + stage * STAGE, bs = as + BM * kBK;
+    const int r0 = (wid * LOADS + (q >> 1)) * 8;
+    if ((q & 1) == 0) dma16(rsa, as + r0 * kBK, past ? ext_a : va, k0 + r0 * lda);
+    else dma16(rsb, bs + r0 * kBK, past ? ext_b : vb, k0 + r0 * ldb);
+  };
+  auto issue_all = [&](int stage, int k0) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r0 = (wid * LOADS + i) * 8;
-      dma16(rsa, as + r0 * kBK, oa, k0 + r0 * lda);
-      dma16(rsb, bs + r0 * kBK, ob, k0 + r0 * ldb);
-    }
+    for (int q = 0; q < 2 * LOADS; ++q) issue_one(stage, k0, q);
   };
 
   v4f acc[TI][TJ];
@@ -280,11 +285,11 @@ __global__ void __launch_bounds__(kBigThreads, 1) mm_fp8_256(MmArgs p, int64_t t
 
   const int nk = (K + kBK - 1) / kBK;
   const int r16 = lane & 15, g = lane >> 4;
-  if (nk > 0) issue(0, 0);
+  if (nk > 0) issue_all(0, 0);
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kBK);
+    if (kt + 1 < nk) issue_all((kt + 1) & 1, (kt + 1) * kBK);
     const uint8_t* As = smem + (kt & 1) * STAGE;
     const uint8_t* Bs = As + BM * kBK;
     v8i bfr[TJ];
@@ -314,6 +319,35 @@ __global__ void __launch_bounds__(kBigThreads, 1) mm_fp8_256(MmArgs p, int64_t t
       const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng + r;
       bias_v[j][r] = (p.bias && gn < p.N) ? load_bias(p.bias, p.bias_dtype, gn) : 0.0f;
     }
+  // Interior tiles go out through LDS (the stages are free after the K loop):
+  // each lane parks its 4-column pieces in a [256][256 + 8] bf16 tile, then
+  // every wave stores whole 512-byte rows with 16-byte lanes.
+  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && (p.ldc % 8) == 0 &&
+                        ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
+  if (interior) {
+    uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int lm = wm * WM + 16 * i + r16;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        uint32_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bias_v[j][r]));
+        *reinterpret_cast<uint2*>(Cs + lm * CROW + wn * WN + 16 * j + 4 * ng) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      }
+    }
+    __syncthreads();
+    // 32 lanes x 16 bytes per row; a wave stores 2 rows per step.
+    const int half = lane >> 5, cl = lane & 31;
+#pragma unroll 4
+    for (int rr = wid * 2 + half; rr < BM; rr += 2 * NWAVES) {
+      const uint4 v = *reinterpret_cast<const uint4*>(Cs + rr * CROW + 8 * cl);
+      *reinterpret_cast<uint4*>(C + (m0 + rr) * p.ldc + n0 + 8 * cl) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     const int64_t gm = m0 + wm * WM + 16 * i + r16;
@@ -348,7 +382,7 @@ template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStre
     const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     const int group_m = 4;
     const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
-    hipLaunchKernelGGL((mm_fp8_256<FA, FB>), grid, dim3(kBigThreads), 0, st, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((mm_fp8_256<FA, FB, 2, 4>), grid, dim3(512), 0, st, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
   }
   constexpr int BM = 128, BN = 128;

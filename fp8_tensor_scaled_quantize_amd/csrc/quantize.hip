@@ -52,6 +52,46 @@ __device__ __forceinline__ void quant_block_done(const QuantArgs& p, float threa
   }
 }
 
+// Running max of |x| over raw 16-byte loads, on the bit patterns: for each
+// input type the bits of |x| order exactly like the magnitudes, and NaNs sort
+// above infinity, so one integer max (packed 16-bit for bf16 / fp16) yields
+// both the amax and whether a NaN was seen.
+template <int DT> struct AbsMax;
+template <> struct AbsMax<kBF16> {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m = {0, 0};
+  __device__ __forceinline__ void add(const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[e] & 0x7FFF7FFFu));
+  }
+  __device__ __forceinline__ uint32_t top() const { return m[0] > m[1] ? m[0] : m[1]; }
+  __device__ __forceinline__ bool has_nan() const { return top() > 0x7F80u; }
+  __device__ __forceinline__ float value() const { return bf16_to_f32(top()); }
+};
+template <> struct AbsMax<kF16> {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m = {0, 0};
+  __device__ __forceinline__ void add(const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[e] & 0x7FFF7FFFu));
+  }
+  __device__ __forceinline__ uint32_t top() const { return m[0] > m[1] ? m[0] : m[1]; }
+  __device__ __forceinline__ bool has_nan() const { return top() > 0x7C00u; }
+  __device__ __forceinline__ float value() const { return f16_to_f32(top()); }
+};
+template <> struct AbsMax<kF32> {
+  uint32_t m = 0;
+  __device__ __forceinline__ void add(const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, w[e] & 0x7FFFFFFFu);
+  }
+  __device__ __forceinline__ bool has_nan() const { return m > 0x7F800000u; }
+  __device__ __forceinline__ float value() const { return __uint_as_float(m); }
+};
+
 // max |v| over the non-NaN values.  The fast loops use v_max_f32, which is
 // not NaN-free when an operand is a signalling NaN (it returns a quiet NaN),
 // so a chunk that holds any NaN recomputes its amax here.
@@ -93,14 +133,11 @@ __device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t
       for (int e = 0; e < 4; ++e) widen2<DT>(w[e], f[j * 8 + 2 * e], f[j * 8 + 2 * e + 1]);
     }
   }
-  bool nan = false;
-  float camax = 0.0f;
+  AbsMax<DT> am;
 #pragma unroll
-  for (int e = 0; e < kFlatElemsPerThread; ++e) {
-    camax = fmaxf(camax, fabsf(f[e]));
-    nan |= f[e] != f[e];
-  }
-  if (nan) camax = nan_free_absmax<kFlatElemsPerThread>(f);
+  for (int j = 0; j < NL; ++j) am.add(v[j]);
+  const bool nan = am.has_nan();
+  const float camax = nan ? nan_free_absmax<kFlatElemsPerThread>(f) : am.value();
   uint32_t code[kFlatElemsPerThread / 4];
   if (!nan) {
 #pragma unroll
@@ -208,21 +245,27 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
     const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
     const int64_t cc = c0 + 8 * cg;  // this thread's first column
     float f[4][8];
+    AbsMax<DT> am;
+    bool all_full = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t r = r0 + 4 * rg + i;
       const char* src = xb + (r * p.ld_x + cc) * EB;
       const bool full = r < p.rows && cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+      all_full &= full;
       if (full) {
         if constexpr (DT == kF32) {
           const uint4 a = reinterpret_cast<const uint4*>(src)[0];
           const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+          am.add(a);
+          am.add(b);
           f[i][0] = __uint_as_float(a.x); f[i][1] = __uint_as_float(a.y);
           f[i][2] = __uint_as_float(a.z); f[i][3] = __uint_as_float(a.w);
           f[i][4] = __uint_as_float(b.x); f[i][5] = __uint_as_float(b.y);
           f[i][6] = __uint_as_float(b.z); f[i][7] = __uint_as_float(b.w);
         } else {
           const uint4 a = *reinterpret_cast<const uint4*>(src);
+          am.add(a);
           widen2<DT>(a.x, f[i][0], f[i][1]); widen2<DT>(a.y, f[i][2], f[i][3]);
           widen2<DT>(a.z, f[i][4], f[i][5]); widen2<DT>(a.w, f[i][6], f[i][7]);
         }
@@ -232,16 +275,19 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
           f[i][e] = (r < p.rows && cc + e < p.cols) ? load1<DT>(p.x, r * p.ld_x + cc + e) : 0.0f;
       }
     }
-    bool nan = false;
-    float camax = 0.0f;
+    bool nan;
+    float camax;
+    if (all_full) {  // every element came through a vector load
+      nan = am.has_nan();
+      camax = nan ? nan_free_absmax<32>(&f[0][0]) : am.value();
+    } else {
+      nan = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        camax = fmaxf(camax, fabsf(f[i][e]));
-        nan |= f[i][e] != f[i][e];
-      }
-    if (nan) camax = nan_free_absmax<32>(&f[0][0]);
+        for (int e = 0; e < 8; ++e) nan |= f[i][e] != f[i][e];
+      camax = nan_free_absmax<32>(&f[0][0]);
+    }
     amax = fmaxf(amax, camax);
     uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
     if (!nan) {

@@ -159,6 +159,31 @@ FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t 
                     const void* bias, int bias_dtype,
                     void* c, int64_t ldc, int64_t stride_c, void* stream);
 
+/*
+ * fp8_bias_grad -- bias gradient of an fp8 linear layer: out[j] = the sum of
+ * dy[i, j] over all rows i (every leading dimension flattened into rows),
+ * accumulated in fp64 in a fixed order and rounded once to bf16
+ * (log:tests/extension, the commit reducing grad_b over leading dims; the
+ * commit forcing gradients to bf16).
+ *   dy   device, element (i, j) at dy[i * ld + j], dy_dtype FP8MI_BF16 or
+ *        FP8MI_F16 (FP8MI_F32 returns FP8MI_ERR_UNSUPPORTED); ld >= cols.
+ *   out  device bf16 [cols].
+ * rows == 0 writes zeros; cols == 0 is a no-op.
+ */
+FP8MI_API fp8mi_status fp8_bias_grad(const void* dy, int dy_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                     void* out, void* stream);
+
+/*
+ * fp8_ring_seed -- (re)initialise a ring on the device: history, ticket and
+ * scratch set to 0, slot 0, and current scale = the scale a fold of *amax
+ * into an empty window would publish (fmt_max / amax, or 1.0 when amax is 0
+ * or not finite).  This is the ring's seed step (log:tests/extension, the
+ * commit giving the scale ring update / seed operations); *amax is typically
+ * the amax_out of a quantize of the first tensor.  ring: device,
+ * FP8MI_RING_WORDS(hist_len) words; amax: device fp32.
+ */
+FP8MI_API fp8mi_status fp8_ring_seed(uint32_t* ring, int32_t hist_len, const float* amax, int fmt, void* stream);
+
 /* Static text of a status code. */
 FP8MI_API const char* fp8mi_status_string(int status);
 /* Thread-local detail of the last non-OK status returned on this thread. */

@@ -86,3 +86,49 @@ def ring_to_oracle(ring: torch.Tensor) -> "O.Ring":
 def ring_from_oracle(r: "O.Ring") -> torch.Tensor:
     w = np.concatenate([r.words(), np.zeros(RING_SCRATCH, np.uint32)])
     return torch.from_numpy(w.view(np.int32).copy()).to(DEV)
+
+
+# ----------------------------------------------------------------- GEMM checks ----
+MFMA_GROUP = 8
+MFMA_GROUP_LOSS = 7 * 2.0 ** -12
+
+
+def mfma_group_term(a, fa, b, fb, sa, sb):
+    """7 * 2^-12 * sum_g max|a_ik| max|b_jk| over aligned groups of 8 k."""
+    da = np.abs(O.decode_table(fa)[a])
+    db = np.abs(O.decode_table(fb)[b])
+    K = a.shape[-1]
+    if K == 0:
+        return np.zeros((a.shape[0], b.shape[0]))
+    ga = da.reshape(a.shape[0], K // MFMA_GROUP, MFMA_GROUP).max(-1)
+    gb = db.reshape(b.shape[0], K // MFMA_GROUP, MFMA_GROUP).max(-1)
+    return MFMA_GROUP_LOSS * (ga @ gb.T) * abs(float(np.float32(sa)) * float(np.float32(sb)))
+
+
+def check(gpu_bits, a, fa, b, fb, sa, sb, bias, rows=None, tag="", exact=False):
+    """Compare (a sample of rows of) the GPU output with the oracle."""
+    a3 = a if a.ndim == 3 else a[None]
+    b3 = b if b.ndim == 3 else b[None]
+    g3 = gpu_bits if gpu_bits.ndim == 3 else gpu_bits[None]
+    batch = max(a3.shape[0], b3.shape[0])
+    n_all = n_stated = 0
+    for z in range(batch):
+        az = a3[min(z, a3.shape[0] - 1)]
+        bz = b3[min(z, b3.shape[0] - 1)]
+        rsel = np.arange(az.shape[0]) if rows is None else rows
+        ref, mag = O.mm(az[rsel], fa, bz, fb, sa, sb, bias)
+        got = g3[z][rsel]
+        if exact:
+            bad = got != ref[0]
+            assert not bad.any(), f"{tag} batch {z}: {bad.sum()} of {bad.size} differ from the exact result"
+            continue
+        stated = O.within_tolerance(got, ref[0], mag[0])
+        ext = O.within_tolerance(got, ref[0], mag[0] + mfma_group_term(az[rsel], fa, bz, fb, sa, sb) / 1e-5)
+        assert ext.all(), f"{tag} batch {z}: {(~ext).sum()} of {ext.size} outside tolerance"
+        n_all += stated.size
+        n_stated += int(stated.sum())
+    if not exact and n_all >= 4096:
+        frac = n_stated / n_all
+        assert frac >= 0.999, f"{tag}: only {frac:.5f} of outputs within the stated bound"
+
+

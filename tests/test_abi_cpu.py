@@ -116,3 +116,24 @@ def test_binding_raises_without_gpu_on_bad_args():
         fp8mi.fp8_quantize(x.t()[:, :3].t() if False else x.unsqueeze(0), fp8mi.E4M3, scale=None)
     with pytest.raises(ValueError):
         fp8mi.fp8_quantize(x, "e9m9", scale=None)
+
+
+def test_bias_grad_rejects(L):
+    f = L.fp8_bias_grad
+    assert f(FAKE, 0, 4, 4, 4, FAKE, None) == UNSUP          # fp32 gradient
+    assert f(FAKE, 9, 4, 4, 4, FAKE, None) == ENUM
+    assert f(FAKE, 2, -1, 4, 4, FAKE, None) == SHAPE
+    assert f(FAKE, 2, 4, 4, 3, FAKE, None) == SHAPE
+    assert f(None, 2, 4, 4, 4, FAKE, None) == NULL
+    assert f(FAKE, 2, 4, 4, 4, None, None) == NULL
+    assert f(FAKE + 1, 2, 4, 4, 4, FAKE, None) == ARG
+    assert f(None, 2, 4, 0, 4, None, None) == OK            # no columns: no-op
+
+
+def test_ring_seed_rejects(L):
+    f = L.fp8_ring_seed
+    assert f(None, 4, FAKE, 0, None) == NULL
+    assert f(FAKE, 4, None, 0, None) == NULL
+    assert f(FAKE, 4, FAKE, 3, None) == ENUM
+    assert f(FAKE, 0, FAKE, 0, None) == SHAPE
+    assert f(FAKE + 2, 4, FAKE, 0, None) == ARG

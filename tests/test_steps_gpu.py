@@ -1,0 +1,166 @@
+"""Delayed-scaling steps through the library against the oracle.
+
+* tiny config: X bf16 [64,256] N(0,1) fresh each step, W [256,256] N(0,0.02),
+  bias [256] N(0,0.1); E4M3 row-layout quantize, 4-entry history; one seeded
+  step and 3 delayed steps.  Codes, scale snapshots and ring words bit-exact,
+  Y within the GEMM bound.
+* checkpoint / resume: a ring is a plain device buffer; 4 + (copy, restore) +
+  4 steps equal 8 straight steps, bit for bit.
+* full training step: x bf16 [4,2048,1536] N(0,1) and dY [8192,6912]
+  N(0,1e-3) fresh each step, W [6912,1536] N(0,0.02) and bias [6912] N(0,0.1)
+  fixed; E4M3 x/W, E5M2 dY, 16-entry histories, 32 steps.  Ring words and
+  scale snapshots bit-exact every step; codes bit-exact on seeded row and
+  column samples every step; Y and dX on sampled rows every step, dW on
+  sampled rows at steps 0, 1, 15, 31; the bias gradient in full every step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import DEV, as_bits, check, np_bf16_bits, np_codes, ring_state_words
+
+pytestmark = pytest.mark.gpu
+
+fp8mi = pytest.importorskip("fp8_tensor_scaled_quantize_amd")
+from fp8_tensor_scaled_quantize_amd.linear import Fp8Linear  # noqa: E402
+
+
+def dev_bf16(bits):
+    return synth.to_torch(bits, "bf16").to(DEV)
+
+
+def f32_words(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def tiny_inputs(steps):
+    xs = [synth.gaussian((64, 256), 1.0, "bf16", 1, synth.T_X, t) for t in range(steps)]
+    w = synth.gaussian((256, 256), 0.02, "bf16", 1, synth.T_W, 0)
+    b = synth.gaussian((256,), 0.1, "bf16", 1, synth.T_BIAS, 0)
+    return xs, w, b
+
+
+def test_tiny_delayed_scaling_steps():
+    xs, w, b = tiny_inputs(4)
+    xs[2] = synth.f32_to_bf16_bits(O.widen_to_f32(xs[2], "bf16") * np.float32(10.0))  # amax jumps 10x
+    rx, rw = O.seed_ring(4, xs[0], "bf16", O.E4M3), O.seed_ring(4, w, "bf16", O.E4M3)
+    layer = Fp8Linear(dev_bf16(w), dev_bf16(b), hist_len=4)
+    layer.seed(dev_bf16(xs[0]))
+    torch.cuda.synchronize()
+    assert np.array_equal(ring_state_words(layer.ring_x), rx.words())
+    assert np.array_equal(ring_state_words(layer.ring_w), rw.words())
+    for t in range(4):
+        ref = O.linear_forward(xs[t], w, b, rx, rw)
+        y = layer.forward(dev_bf16(xs[t]), save_for_backward=False)
+        xq, wq = layer.last_codes
+        torch.cuda.synchronize()
+        assert np.array_equal(np_codes(xq), ref["qx"]["codes"]), t
+        assert np.array_equal(np_codes(wq), ref["qw"]["codes"]), t
+        si = f32_words(layer.scale_inv)
+        assert si[0] == as_bits(ref["qx"]["scale_inv"]) and si[1] == as_bits(ref["qw"]["scale_inv"]), t
+        rx, rw = ref["qx"]["ring"], ref["qw"]["ring"]
+        assert np.array_equal(ring_state_words(layer.ring_x), rx.words()), t
+        assert np.array_equal(ring_state_words(layer.ring_w), rw.words()), t
+        bias = O.widen_to_f32(b, "bf16").astype(np.float64)
+        check(np_bf16_bits(y), ref["qx"]["codes"], O.E4M3, ref["qw"]["codes"], O.E4M3,
+              ref["qx"]["scale_inv"], ref["qw"]["scale_inv"], bias, tag=f"tiny step {t}")
+    # the step after the jump quantized with the stale (delayed) scale and the
+    # GEMM dequantised with that same snapshot: no leak of the scale ratio
+    assert rx.scale < np.float32(448.0) / O.amax(O.widen_to_f32(xs[1], "bf16"))
+
+
+def test_checkpoint_resume_rings():
+    xs, w, b = tiny_inputs(8)
+    straight = Fp8Linear(dev_bf16(w), dev_bf16(b), hist_len=3)
+    straight.seed(dev_bf16(xs[0]))
+    ys = [straight.forward(dev_bf16(x), save_for_backward=False).clone() for x in xs]
+
+    first = Fp8Linear(dev_bf16(w), dev_bf16(b), hist_len=3)
+    first.seed(dev_bf16(xs[0]))
+    ys2 = [first.forward(dev_bf16(x), save_for_backward=False).clone() for x in xs[:4]]
+    saved = [first.ring_x.cpu().clone(), first.ring_w.cpu().clone()]       # checkpoint = byte copy
+    resumed = Fp8Linear(dev_bf16(w), dev_bf16(b), hist_len=3)
+    resumed.ring_x.copy_(saved[0].to(DEV))
+    resumed.ring_w.copy_(saved[1].to(DEV))
+    ys2 += [resumed.forward(dev_bf16(x), save_for_backward=False).clone() for x in xs[4:]]
+    torch.cuda.synchronize()
+    for a, c in zip(ys, ys2):
+        assert torch.equal(a, c)
+    assert torch.equal(straight.ring_x, resumed.ring_x) and torch.equal(straight.ring_w, resumed.ring_w)
+
+
+@pytest.mark.timeout(900)
+def test_full_training_step_32_steps():
+    M, K, N, H, STEPS = 8192, 1536, 6912, 16, 32
+    w = synth.gaussian((N, K), 0.02, "bf16", 5, synth.T_W, 0)
+    b = synth.gaussian((N,), 0.1, "bf16", 5, synth.T_BIAS, 0)
+    wf, bias = O.widen_to_f32(w, "bf16"), O.widen_to_f32(b, "bf16").astype(np.float64)
+    layer = Fp8Linear(dev_bf16(w), dev_bf16(b), hist_len=H)
+
+    def x_of(t):
+        return synth.gaussian((M, K), 1.0, "bf16", 5, synth.T_X, t)
+
+    def dy_of(t):
+        return synth.gaussian((M, N), 1e-3, "bf16", 5, synth.T_DY, t)
+
+    x0, dy0 = x_of(0), dy_of(0)
+    rx = O.seed_ring(H, x0, "bf16", O.E4M3)
+    rw = O.seed_ring(H, w, "bf16", O.E4M3)
+    rg = O.seed_ring(H, dy0, "bf16", O.E5M2)
+    layer.seed(dev_bf16(x0).view(4, 2048, K), dev_bf16(dy0))
+    w_codes = {}
+
+    for t in range(STEPS):
+        x = x0 if t == 0 else x_of(t)
+        dy = dy0 if t == 0 else dy_of(t)
+        y = layer.forward(dev_bf16(x).view(4, 2048, K))
+        dx, dw, db = layer.backward(dev_bf16(dy))
+        torch.cuda.synchronize()
+        xf, gf = O.widen_to_f32(x, "bf16"), O.widen_to_f32(dy, "bf16")
+        sx, sw, sg = rx.scale, rw.scale, rg.scale
+        rx = O.fold(rx, O.amax(xf), O.E4M3)
+        rw = O.fold(rw, O.amax(wf), O.E4M3)
+        rg = O.fold(rg, O.amax(gf), O.E5M2)
+        for ring, ref in ((layer.ring_x, rx), (layer.ring_w, rw), (layer.ring_g, rg)):
+            assert np.array_equal(ring_state_words(ring), ref.words()), t
+        si = f32_words(layer.scale_inv)
+        assert list(si) == [as_bits(O.scale_inv(s)) for s in (sx, sw, sg)], t
+
+        # codes on seeded samples of rows (row layout) and columns (transposed layout)
+        rs = np.sort(synth.rng(6, t, 0).choice(M, 48, replace=False))
+        cs_k = np.sort(synth.rng(6, t, 1).choice(K, 24, replace=False))
+        cs_n = np.sort(synth.rng(6, t, 2).choice(N, 24, replace=False))
+        xq_rows = O.encode(O.scaled_values(xf[rs], sx), O.E4M3)
+        gq_rows = O.encode(O.scaled_values(gf[rs], sg), O.E5M2)
+        xq, wq = layer.last_codes
+        gq, gq_t = layer.last_grad_codes
+        xq_t_dev, wq_t_dev, _ = layer._saved
+        assert np.array_equal(np_codes(xq[rs]), xq_rows), t
+        assert np.array_equal(np_codes(gq[rs]), gq_rows), t
+        assert np.array_equal(np_codes(xq_t_dev[cs_k]), O.encode(O.scaled_values(xf[:, cs_k], sx), O.E4M3).T), t
+        assert np.array_equal(np_codes(gq_t[cs_n]), O.encode(O.scaled_values(gf[:, cs_n], sg), O.E5M2).T), t
+        key = as_bits(sw)
+        if key not in w_codes:
+            w_codes[key] = O.encode(O.scaled_values(wf, sw), O.E4M3)
+            assert np.array_equal(np_codes(wq), w_codes[key]), t
+            assert np.array_equal(np_codes(wq_t_dev), w_codes[key].T), t
+        wc = w_codes[key]
+
+        # GEMMs on sampled rows: each sampled output row is exact in the oracle
+        y2 = np_bf16_bits(y.reshape(M, N))
+        check(y2[rs], xq_rows, O.E4M3, wc, O.E4M3, O.scale_inv(sx), O.scale_inv(sw), bias, tag=f"Y step {t}")
+        check(np_bf16_bits(dx.reshape(M, K))[rs], gq_rows, O.E5M2, np.ascontiguousarray(wc.T), O.E4M3,
+              O.scale_inv(sg), O.scale_inv(sw), None, tag=f"dX step {t}")
+        if t in (0, 1, 15, 31):
+            xq_t_full = np.ascontiguousarray(O.encode(O.scaled_values(xf, sx), O.E4M3).T)
+            ns = np.sort(synth.rng(6, t, 3).choice(N, 24, replace=False))
+            gq_t_rows = np.ascontiguousarray(O.encode(O.scaled_values(gf[:, ns], sg), O.E5M2).T)
+            check(np_bf16_bits(dw)[ns], gq_t_rows, O.E5M2, xq_t_full, O.E4M3, O.scale_inv(sg), O.scale_inv(sx),
+                  None, tag=f"dW step {t}")
+        # bias gradient: full
+        db_ref, db_mag = O.grad_bias(dy)
+        db_gpu = np_bf16_bits(db)
+        assert O.within_tolerance(db_gpu, db_ref, db_mag).all(), t
+        assert (db_gpu == db_ref).mean() > 0.999, t
