@@ -82,6 +82,63 @@ def cpu_baseline(seconds_target=8.0):
             "quantize_GBps": round(q_gbs, 4), "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def kernel_source_hash():
+    """sha256 of the HIP sources: counters taken on other sources are stale."""
+    import hashlib
+    csrc = os.path.join(ROOT, "fp8_tensor_scaled_quantize_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """Per-launch HBM bytes {kernel: {"fetch": B, "write": B}} from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when it was
+    taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("kernels")
+
+
+def time_training_step(torch, fp8mi, synth, steps, warmup):
+    """The full fp8 linear training step at the 1.2B-model FFN shape: x bf16
+    [4,2048,1536], W [6912,1536], bias, dY [8192,6912]; dual quantize x, W
+    (E4M3) and dY (E5M2) with 16-entry rings, Y, dX, dW GEMMs, bias grad."""
+    from fp8_tensor_scaled_quantize_amd.linear import Fp8Linear
+    dev = torch.device("cuda:0")
+    M, K, N = 8192, 1536, 6912
+    w = synth.device_gaussian((N, K), 0.02, torch.bfloat16, 5000, dev)
+    b = synth.device_gaussian((N,), 0.1, torch.bfloat16, 5001, dev)
+    xs = [synth.device_gaussian((4, 2048, K), 1.0, torch.bfloat16, 5100 + i, dev) for i in range(3)]
+    dys = [synth.device_gaussian((M, N), 1e-3, torch.bfloat16, 5200 + i, dev) for i in range(3)]
+    layer = Fp8Linear(w, b, hist_len=HIST)
+    layer.seed(xs[0], dys[0])
+    for s in range(warmup):
+        layer.forward(xs[s % 3])
+        layer.backward(dys[s % 3])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        layer.forward(xs[s % 3])
+        layer.backward(dys[s % 3])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 3 * 2.0 * M * N * K
+    return {"workload": "fp8 linear fwd+bwd, x [4,2048,1536], W [6912,1536], dY [8192,6912], H=16",
+            "ms_per_step": round(ms, 4), "gemm_TFLOPs_over_step": round(flops / (ms * 1e-3) / 1e12, 1),
+            "launches_per_step": 8}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -203,6 +260,15 @@ def main():
                               "kernel": "quantize_dual"},
         "quantize": quant,
     }
+    traffic = counter_traffic()
+    if traffic:
+        for key, name in (("roofline", "mm_fp8"), ("roofline_quantize", "quantize_dual")):
+            t = traffic.get(name)
+            if t:
+                out[key]["traffic"] = int(t["fetch"] + t["write"])
+                out[key]["traffic_fetch"] = int(t["fetch"])
+                out[key]["traffic_write"] = int(t["write"])
+    out["training_step"] = time_training_step(torch, fp8mi, synth, max(3, args.steps // 5), 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
