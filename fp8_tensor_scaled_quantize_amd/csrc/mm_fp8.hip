@@ -20,6 +20,8 @@
 #include "fp8mi_device.h"
 #include "fp8mi_internal.h"
 
+#include <cstdlib>
+
 namespace fp8mi {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -231,15 +233,17 @@ __device__ __forceinline__ void tile_coords(int64_t wg, int64_t tiles_m, int64_t
   tn = r / rows_here;
 }
 
-template <int FA, int FB, int WAVES_M, int WAVES_N>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) mm_fp8_256(MmArgs p, int64_t tiles_m, int64_t tiles_n,
-                                                                        int group_m) {
-  constexpr int BM = 256, BN = 256;
+template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma(MmArgs p, int64_t tiles_m,
+                                                                                 int64_t tiles_n, int group_m) {
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TI = WM / 16, TJ = WN / 16;
   constexpr int STAGE = (BM + BN) * kBK;      // bytes per LDS stage
-  constexpr int LOADS = BM / 8 / NWAVES;      // 1 KiB load instructions per wave per operand
+  constexpr int LA = BM / 8 / NWAVES;         // 1 KiB load instructions per wave for A
+  constexpr int LB = BN / 8 / NWAVES;         // ... and for B
+  static_assert(LA >= 1 && LB >= 1 && LA * 8 * NWAVES == BM && LB * 8 * NWAVES == BN, "tile / wave mismatch");
+  static_assert(TI >= 1 && TJ >= 1, "wave tile below one MFMA tile");
   constexpr int CROW = BN + 8;                // bf16 per LDS row of the staged C tile (16 B pad)
   constexpr int SMEM = 2 * STAGE > BM * CROW * 2 ? 2 * STAGE : BM * CROW * 2;
   __shared__ __align__(16) uint8_t smem[SMEM];
@@ -263,18 +267,23 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) mm_fp8_256(MmArgs p
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
 
   // Issue one stage of loads (this wave's 4 + 4 instructions).
-  // Load instruction q (0 .. 2*LOADS-1) of one stage: even q -> A, odd q -> B,
-  // rows (wid * LOADS + q / 2) * 8 .. + 7.
-  auto issue_one = [&](int stage, int k0, int q) {
+  // One stage of loads: this wave's LA instructions for A rows
+  // (wid * LA + q) * 8 .. + 7 and LB for B rows (wid * LB + q) * 8 .. + 7.
+  auto issue_all = [&](int stage, int k0) {
     const bool past = k0 + 16 * lc >= K;  // K tail: chunks at or past K read as zero
     const uint32_t as = smem_lds + stage * STAGE, bs = as + BM * kBK;
-    const int r0 = (wid * LOADS + (q >> 1)) * 8;
-    if ((q & 1) == 0) dma16(rsa, as + r0 * kBK, past ? ext_a : va, k0 + r0 * lda);
-    else dma16(rsb, bs + r0 * kBK, past ? ext_b : vb, k0 + r0 * ldb);
-  };
-  auto issue_all = [&](int stage, int k0) {
+    const int oa = past ? ext_a : va, ob = past ? ext_b : vb;
 #pragma unroll
-    for (int q = 0; q < 2 * LOADS; ++q) issue_one(stage, k0, q);
+    for (int q = 0; q < (LA > LB ? LA : LB); ++q) {
+      if (q < LA) {
+        const int r0 = (wid * LA + q) * 8;
+        dma16(rsa, as + r0 * kBK, oa, k0 + r0 * lda);
+      }
+      if (q < LB) {
+        const int r0 = (wid * LB + q) * 8;
+        dma16(rsb, bs + r0 * kBK, ob, k0 + r0 * ldb);
+      }
+    }
   };
 
   v4f acc[TI][TJ];
@@ -339,10 +348,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) mm_fp8_256(MmArgs p
       }
     }
     __syncthreads();
-    // 32 lanes x 16 bytes per row; a wave stores 2 rows per step.
-    const int half = lane >> 5, cl = lane & 31;
+    // BN / 8 lanes x 16 bytes per row; a wave stores 64 / (BN / 8) rows per step.
+    constexpr int LPR = BN / 8, RPW = 64 / LPR;
+    const int sub = lane / LPR, cl = lane % LPR;
 #pragma unroll 4
-    for (int rr = wid * 2 + half; rr < BM; rr += 2 * NWAVES) {
+    for (int rr = wid * RPW + sub; rr < BM; rr += RPW * NWAVES) {
       const uint4 v = *reinterpret_cast<const uint4*>(Cs + rr * CROW + 8 * cl);
       *reinterpret_cast<uint4*>(C + (m0 + rr) * p.ldc + n0 + 8 * cl) = v;
     }
@@ -371,19 +381,38 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) mm_fp8_256(MmArgs p
   }
 }
 
-// Tile dispatch: the 256 x 256 kernel when the problem fills the machine
-// with it (batch x tiles >= CU count); the 128 x 128 kernel otherwise.
+// Tile dispatch (measured on MI355X over the shapes of the test configs):
+// the 256x256 / 8-wave kernel whenever its tiles (x batch) cover at least 60%
+// of the CUs -- one round of big tiles beats several rounds of small ones even
+// with a quarter of the CUs idle -- and the 64x128 / 4-wave kernel (two per
+// CU) below that, where it beat 128x128 on every shape measured.  128x128 is
+// reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128 kernel
+// remains for operands whose byte extent does not fit a 32-bit buffer offset.
+template <int FA, int FB, int BM, int BN, int WM_, int WN_, int MINB>
+static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
+  const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
+  hipLaunchKernelGGL((mm_fp8_dma<FA, FB, BM, BN, WM_, WN_, MINB>), grid, dim3(64 * WM_ * WN_), 0, st, p, tiles_m,
+                     tiles_n, 4);
+  return hipGetLastError();
+}
+
+static int pick_tile(const MmArgs& p, int ncu) {
+  static const int forced = [] { const char* e = getenv("FP8MI_MM_TILE"); return e ? atoi(e) : -1; }();
+  if (forced >= 0 && forced < 3) return forced;
+  const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+  return 10 * t256 >= 6 * (int64_t)ncu ? 0 : 2;
+}
+
 template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStream_t st) {
-  const int ncu = device_cu_count();
-  const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
   // buffer offsets are 32-bit: extent + largest soffset must stay below 2^32
   const bool fits31 = p.a_extent_from(0) < (1ll << 31) && p.b_extent_from(0) < (1ll << 31) && p.K < (1ll << 30);
-  if (t256 * p.batch >= ncu && fits31) {
-    const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
-    const int group_m = 4;
-    const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
-    hipLaunchKernelGGL((mm_fp8_256<FA, FB, 2, 4>), grid, dim3(512), 0, st, p, tiles_m, tiles_n, group_m);
-    return hipGetLastError();
+  if (fits31) {
+    switch (pick_tile(p, device_cu_count())) {
+      case 0: return launch_dma<FA, FB, 256, 256, 2, 4, 1>(p, st);
+      case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2>(p, st);
+      default: return launch_dma<FA, FB, 64, 128, 1, 4, 2>(p, st);
+    }
   }
   constexpr int BM = 128, BN = 128;
   const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.batch);
