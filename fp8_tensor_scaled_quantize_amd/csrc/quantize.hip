@@ -13,16 +13,20 @@
 // MI355X shape of the kernels (not the pages' sm_89 one):
 //  * quantize_flat: contiguous row layout; each wave moves 64 x 16-byte loads
 //    per step (one contiguous 1 KiB segment per load instruction) and writes
-//    one contiguous segment of codes per store instruction.
+//    one contiguous segment of codes per store instruction.  Persistent
+//    workgroups, the next group of steps loading while one is encoded.
 //  * quantize_tiled: 128-row x 64-column tiles, 256 threads.  Each thread
 //    loads a 4-row x 8-column micro block (16-byte loads where aligned), so
 //    the row-layout codes leave straight from registers and the transposed
 //    codes need only a 4x4 byte transpose in registers plus one 8 KiB LDS
 //    pass, after which every lane stores 16 contiguous bytes of a transposed
-//    row (128-byte segments per 8 lanes).
+//    row (128-byte segments per 8 lanes).  Persistent workgroups, the next
+//    tile loading while one is encoded.
 //  * amax: wave shuffle reduction, one device-scope atomic max per workgroup.
 #include "fp8mi_device.h"
 #include "fp8mi_internal.h"
+
+#include <cstdlib>
 
 namespace fp8mi {
 
@@ -157,38 +161,65 @@ __device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t
   return camax;
 }
 
-// Each block handles `steps_per_block` consecutive block steps, kFlatUnroll at
-// a time with all of their loads issued before any is consumed.
-template <int DT, int FMT>
+// Each block handles `steps_per_block` consecutive block steps in groups of
+// kFlatUnroll.  With PF the groups are software-pipelined over two register
+// buffers (the loads of group g + 1 in flight while group g is encoded), for
+// persistent grids over large tensors; without it a block holds one group
+// at a time, which keeps registers low and occupancy high for the grids that
+// give every workgroup a single group.
+template <int DT, int FMT, bool PF>
 __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64_t n, int64_t steps_per_block) {
   __shared__ float red[kFlatThreads / 64];
   constexpr int EB = In<DT>::kBytes;
   constexpr int EPL = 16 / EB;                   // elements per 16-byte load
   constexpr int NL = kFlatElemsPerThread / EPL;  // loads per lane per step
-  const float s = read_scale<FMT>(p);
+  constexpr int U = kFlatUnroll;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   float amax = 0.0f;
   const char* xb = static_cast<const char*>(p.x);
   const int64_t first = (int64_t)blockIdx.x * steps_per_block;
   const int64_t total_steps = (n + kFlatBlockStep - 1) / kFlatBlockStep;
   const int64_t last = first + steps_per_block < total_steps ? first + steps_per_block : total_steps;
-  int64_t st = first;
-  // full unrolled groups: every wave step of the group lies inside the tensor
-  for (; st + kFlatUnroll <= last && (st + kFlatUnroll) * kFlatBlockStep <= n; st += kFlatUnroll) {
-    uint4 v[kFlatUnroll][NL];
+  // groups of U steps that lie wholly inside the tensor
+  const int64_t full_end = last < n / kFlatBlockStep ? last : n / kFlatBlockStep;
+  const int64_t ng = full_end > first ? (full_end - first) / U : 0;
+  auto load_group = [&](uint4 (&v)[U][NL], int64_t g0) {
 #pragma unroll
-    for (int u = 0; u < kFlatUnroll; ++u) {
-      const int64_t w0 = (st + u) * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
+    for (int u = 0; u < U; ++u) {
+      const int64_t w0 = (g0 + u) * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
 #pragma unroll
       for (int j = 0; j < NL; ++j)
         v[u][j] = *reinterpret_cast<const uint4*>(xb + (w0 + (int64_t)(j * 64 + lane) * EPL) * EB);
     }
+  };
+  uint4 va[U][NL];
+  if (ng > 0) load_group(va, first);
+  // the scale is read after the first loads are out (it does not gate them)
+  const float s = read_scale<FMT>(p);
+  auto encode_group = [&](const uint4 (&v)[U][NL], int64_t g0) {
 #pragma unroll
-    for (int u = 0; u < kFlatUnroll; ++u) {
-      const int64_t w0 = (st + u) * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
+    for (int u = 0; u < U; ++u) {
+      const int64_t w0 = (g0 + u) * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
       amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v[u], p.out_row + w0, lane, s));
     }
+  };
+  int64_t g = 0;
+  if constexpr (PF) {
+    uint4 vb[U][NL];
+    for (; g + 2 <= ng; g += 2) {
+      load_group(vb, first + (g + 1) * U);
+      encode_group(va, first + g * U);
+      if (g + 2 < ng) load_group(va, first + (g + 2) * U);
+      encode_group(vb, first + (g + 1) * U);
+    }
+  } else {
+    for (; g + 1 < ng; ++g) {
+      encode_group(va, first + g * U);
+      load_group(va, first + (g + 1) * U);
+    }
   }
+  if (g < ng) encode_group(va, first + g * U);
+  int64_t st = first + ng * U;
   for (; st < last; ++st) {
     const int64_t w0 = st * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
     if (w0 + kFlatWaveStep <= n) {
@@ -229,6 +260,8 @@ enum Mode : int { kRow = 0, kTrans = 1, kDual = 2 };
 
 __device__ __forceinline__ int lds_t_index(int c, int w) { return c * 32 + (w ^ (8 * ((c >> 3) & 3))); }
 
+// One-shot form: each workgroup loads, encodes and stores its tiles in turn
+// (launched with one tile per workgroup; low registers, high occupancy).
 template <int DT, int FMT, int MODE>
 __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int64_t tiles_c, int64_t ntiles,
                                                                 int64_t tiles_per_block) {
@@ -356,6 +389,169 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
   quant_block_done<FMT, kTileThreads>(p, amax, s, red);
 }
 
+// Persistent form (quantize_tiled_pf).  One tile's raw input for this thread: rows 4rg..4rg+3 at columns
+// 8cg..8cg+7, as 16-byte loads (two per row for f32) where the row lies
+// inside the tensor with a 16-byte aligned start; other rows are read
+// element by element while the tile is processed.
+template <int DT> struct TileRaw {
+  static constexpr int kLoads = In<DT>::kBytes == 4 ? 2 : 1;
+  uint4 v[4][kLoads];
+  uint32_t full;  // bit i: row i came through vector loads
+};
+
+template <int DT, int FMT, int MODE>
+__global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, int64_t tiles_c, int64_t ntiles,
+                                                                int64_t tiles_per_block) {
+  __shared__ float red[kTileThreads / 64];
+  __shared__ __align__(16) uint32_t lds_t[(MODE == kRow) ? 1 : kTileC * 32];
+  constexpr int EB = In<DT>::kBytes;
+  constexpr int NLD = TileRaw<DT>::kLoads;
+  const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
+  float amax = 0.0f;
+  const char* xb = static_cast<const char*>(p.x);
+  const int64_t t_first = (int64_t)blockIdx.x * tiles_per_block;
+  const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
+
+  auto load_tile = [&](int64_t tile, TileRaw<DT>& L) {
+    const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
+    const int64_t cc = c0 + 8 * cg;
+    L.full = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * rg + i;
+      const char* src = xb + (r * p.ld_x + cc) * EB;
+      const bool full = r < p.rows && cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+      L.full |= (uint32_t)full << i;
+      if (full) {
+#pragma unroll
+        for (int q = 0; q < NLD; ++q) L.v[i][q] = reinterpret_cast<const uint4*>(src)[q];
+      }
+    }
+  };
+
+  auto process_tile = [&](int64_t tile, const TileRaw<DT>& L, float s) {
+    const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
+    const int64_t cc = c0 + 8 * cg;  // this thread's first column
+    float f[4][8];
+    AbsMax<DT> am;
+    const bool all_full = L.full == 0xFu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * rg + i;
+      if ((L.full >> i) & 1u) {
+        if constexpr (DT == kF32) {
+          const uint4 a = L.v[i][0], b = L.v[i][NLD - 1];
+          am.add(a);
+          am.add(b);
+          f[i][0] = __uint_as_float(a.x); f[i][1] = __uint_as_float(a.y);
+          f[i][2] = __uint_as_float(a.z); f[i][3] = __uint_as_float(a.w);
+          f[i][4] = __uint_as_float(b.x); f[i][5] = __uint_as_float(b.y);
+          f[i][6] = __uint_as_float(b.z); f[i][7] = __uint_as_float(b.w);
+        } else {
+          const uint4 a = L.v[i][0];
+          am.add(a);
+          widen2<DT>(a.x, f[i][0], f[i][1]); widen2<DT>(a.y, f[i][2], f[i][3]);
+          widen2<DT>(a.z, f[i][4], f[i][5]); widen2<DT>(a.w, f[i][6], f[i][7]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          f[i][e] = (r < p.rows && cc + e < p.cols) ? load1<DT>(p.x, r * p.ld_x + cc + e) : 0.0f;
+      }
+    }
+    bool nan;
+    float camax;
+    if (all_full) {  // every element came through a vector load
+      nan = am.has_nan();
+      camax = nan ? nan_free_absmax<32>(&f[0][0]) : am.value();
+    } else {
+      nan = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nan |= f[i][e] != f[i][e];
+      camax = nan_free_absmax<32>(&f[0][0]);
+    }
+    amax = fmaxf(amax, camax);
+    uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
+    if (!nan) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          rw[i][h] = cvt4<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s, f[i][4 * h + 3] * s);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          rw[i][h] = enc4_exact<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
+                                     f[i][4 * h + 3] * s);
+    }
+
+    if constexpr (MODE == kRow || MODE == kDual) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + 4 * rg + i;
+        if (r >= p.rows) continue;
+        uint8_t* dst = p.out_row + r * p.ld_row + cc;
+        if (cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(rw[i][0], rw[i][1]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (cc + e < p.cols) dst[e] = (uint8_t)(rw[i][e >> 2] >> (8 * (e & 3)));
+        }
+      }
+    }
+
+    if constexpr (MODE == kTrans || MODE == kDual) {
+      // 4x8 bytes -> 8 column words (rows 4rg..4rg+3 of column 8cg+e)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int h = e >> 2, sh = 8 * (e & 3);
+        const uint32_t col = ((rw[0][h] >> sh) & 0xFFu) | (((rw[1][h] >> sh) & 0xFFu) << 8) |
+                             (((rw[2][h] >> sh) & 0xFFu) << 16) | (((rw[3][h] >> sh) & 0xFFu) << 24);
+        lds_t[lds_t_index(8 * cg + e, rg)] = col;
+      }
+      __syncthreads();
+      // 64 transposed rows (one per input column) x 128 bytes; lane: row cl, 16 bytes at 16q
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int cl = (t >> 3) + 32 * pass, q = t & 7;
+        const int64_t c = c0 + cl;
+        const int64_t rr = r0 + 16 * q;
+        if (c < p.cols && rr < p.rows) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&lds_t[lds_t_index(cl, 4 * q)]);
+          uint8_t* dst = p.out_t + c * p.ld_t + rr;
+          if (rr + 16 <= p.rows && ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0)) {
+            *reinterpret_cast<uint4*>(dst) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (rr + e < p.rows) dst[e] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+          }
+        }
+      }
+      __syncthreads();  // LDS reused by the next tile
+    }
+  };
+
+  // The tiles are software-pipelined: the loads of tile k + 1 are in flight
+  // while tile k is encoded and stored (the copy at the end of an iteration
+  // waits only for that prefetch).
+  TileRaw<DT> cur, nxt;
+  if (t_first < t_last) load_tile(t_first, cur);
+  const float s = read_scale<FMT>(p);  // after the first loads are out
+  for (int64_t tile = t_first; tile < t_last; ++tile) {
+    if (tile + 1 < t_last) load_tile(tile + 1, nxt);
+    process_tile(tile, cur, s);
+    cur = nxt;
+  }
+  quant_block_done<FMT, kTileThreads>(p, amax, s, red);
+}
+
 // Fold alone / arming of a ring-less amax output.
 template <int FMT> __global__ void amax_fold_kernel(uint32_t* ring, int H, const float* amax) {
   if (threadIdx.x < 64) ring_fold_wave<FMT>(ring, H, *amax, nullptr, 1.0f, nullptr);
@@ -369,44 +565,60 @@ __global__ void zero_word_kernel(float* p) {
 // ===========================================================================
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Persistent grids: at most this many workgroups per CU; each loops over an
-// equal share of the work (fewer workgroups -> fewer cross-XCD atomics).
-constexpr int kFlatBlocksPerCU = 8;
-constexpr int kTileBlocksPerCU = 8;
+// Grids (measured on MI355X, kernel trace, bf16 8192 x 1536 and 8192 x 6912):
+// while every workgroup can take a single group / tile within
+// kOneShotBlocksPerCU workgroups per CU, the one-shot kernels run (low
+// registers, everything in flight at once); larger tensors go to persistent
+// workgroups, kPersistBlocksPerCU per CU, each streaming a contiguous share
+// with the next group / tile in flight.  FP8MI_Q_BPC overrides the
+// persistent count for tuning.
+constexpr int kOneShotBlocksPerCU = 8;
+constexpr int kPersistBlocksPerCU = 3;
+static int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+
+template <int DT, int FMT, int M>
+static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantArgs& p, int64_t tiles_c,
+                         int64_t ntiles, int64_t tpb) {
+  if (one_shot) {
+    hipLaunchKernelGGL((quantize_tiled<DT, FMT, M>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
+  } else {
+    hipLaunchKernelGGL((quantize_tiled_pf<DT, FMT, M>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
+  }
+}
 
 template <int DT, int FMT>
 static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int ncu = device_cu_count();
+  static const int persist_bpc = env_int("FP8MI_Q_BPC", kPersistBlocksPerCU);
   const int64_t n = p.rows * p.cols;
   const bool contiguous_row = mode == kRow && p.ld_x == p.cols && p.ld_row == p.cols &&
                               (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
                               (reinterpret_cast<uintptr_t>(p.out_row) & 15u) == 0;
   if (contiguous_row || n == 0) {
     const int64_t steps = cdiv(n, kFlatBlockStep);
-    const int64_t max_blocks = (int64_t)ncu * kFlatBlocksPerCU;
-    const int64_t spb = steps <= max_blocks ? 1 : cdiv(steps, max_blocks);
-    const int64_t blocks = steps == 0 ? 1 : cdiv(steps, spb);
-    hipLaunchKernelGGL((quantize_flat<DT, FMT>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n, spb);
+    if (steps <= (int64_t)ncu * kOneShotBlocksPerCU * kFlatUnroll) {
+      const int64_t spb = kFlatUnroll, blocks = steps == 0 ? 1 : cdiv(steps, spb);
+      hipLaunchKernelGGL((quantize_flat<DT, FMT, false>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n,
+                         spb);
+    } else {
+      const int64_t spb = cdiv(steps, (int64_t)ncu * persist_bpc), blocks = cdiv(steps, spb);
+      hipLaunchKernelGGL((quantize_flat<DT, FMT, true>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n,
+                         spb);
+    }
     return hipGetLastError();
   }
   const int64_t tiles_c = cdiv(p.cols, kTileC);
   const int64_t ntiles = cdiv(p.rows, kTileR) * tiles_c;
-  const int64_t max_blocks = (int64_t)ncu * kTileBlocksPerCU;
-  const int64_t tpb = ntiles <= max_blocks ? 1 : cdiv(ntiles, max_blocks);
-  const int64_t blocks = cdiv(ntiles, tpb);
+  const bool one_shot = ntiles <= (int64_t)ncu * kOneShotBlocksPerCU;
+  const int64_t tpb = one_shot ? 1 : cdiv(ntiles, (int64_t)ncu * persist_bpc);
+  const dim3 grid((unsigned)cdiv(ntiles, tpb));
   switch (mode) {
-    case kRow:
-      hipLaunchKernelGGL((quantize_tiled<DT, FMT, kRow>), dim3((unsigned)blocks), dim3(kTileThreads), 0, st, p,
-                         tiles_c, ntiles, tpb);
-      break;
-    case kTrans:
-      hipLaunchKernelGGL((quantize_tiled<DT, FMT, kTrans>), dim3((unsigned)blocks), dim3(kTileThreads), 0, st, p,
-                         tiles_c, ntiles, tpb);
-      break;
-    default:
-      hipLaunchKernelGGL((quantize_tiled<DT, FMT, kDual>), dim3((unsigned)blocks), dim3(kTileThreads), 0, st, p,
-                         tiles_c, ntiles, tpb);
-      break;
+    case kRow: launch_tiled<DT, FMT, kRow>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
+    case kTrans: launch_tiled<DT, FMT, kTrans>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
+    default: launch_tiled<DT, FMT, kDual>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
   }
   return hipGetLastError();
 }
