@@ -14,7 +14,7 @@ import torch
 from ._lib import lib
 
 __all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual",
-           "fp8_amax_fold", "fp8_mm", "fp8_bias_grad", "fp8_ring_seed", "new_ring", "ring_words", "version"]
+           "fp8_amax_fold", "fp8_mm", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
 
 E4M3, E5M2 = 0, 1
 F32, F16, BF16 = 0, 1, 2
@@ -185,9 +185,18 @@ def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_inv
     return out
 
 
-def fp8_bias_grad(dy: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+def fp8_bias_grad_workspace_bytes(rows: int, cols: int) -> int:
+    """Device workspace fp8_bias_grad needs for a [rows, cols] gradient."""
+    return int(lib().fp8_bias_grad_workspace_bytes(rows, cols))
+
+
+def fp8_bias_grad(dy: torch.Tensor, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Bias gradient: sum of a bf16/fp16 gradient over every leading
-    dimension (fp64 accumulation, one bf16 rounding) -> bf16 [cols]."""
+    dimension (fp64 accumulation in a fixed order, one bf16 rounding) ->
+    bf16 [cols].  `workspace` (any dtype, device) is scratch of at least
+    fp8_bias_grad_workspace_bytes(rows, cols) bytes; one is allocated from
+    torch's caching allocator when it is not given."""
     if dy.dim() < 1 or (dy.shape[-1] > 1 and dy.stride(-1) != 1):
         raise ValueError("dy needs unit stride along its last dimension")
     cols = dy.shape[-1]
@@ -196,7 +205,12 @@ def fp8_bias_grad(dy: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     ld = d2.stride(0) if rows > 1 else cols
     if out is None:
         out = torch.empty(cols, dtype=torch.bfloat16, device=dy.device)
-    _check(lib().fp8_bias_grad(_ptr(d2), _DT[dy.dtype], rows, cols, ld, _ptr(out), _stream(dy)))
+    need = fp8_bias_grad_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dy.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fp8_bias_grad(_ptr(d2), _DT[dy.dtype], rows, cols, ld, _ptr(out), _ptr(workspace), nbytes,
+                               _stream(dy)))
     return out
 
 

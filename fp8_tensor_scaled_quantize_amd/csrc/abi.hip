@@ -168,8 +168,12 @@ fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, 
   return from_hip(launch_mm(p, fmt_a, fmt_b, static_cast<hipStream_t>(stream)), "mm launch");
 }
 
+size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols) {
+  return (size_t)fp8mi::grad_bias_workspace_bytes(rows, cols);
+}
+
 fp8mi_status fp8_bias_grad(const void* dy, int dy_dtype, int64_t rows, int64_t cols, int64_t ld, void* out,
-                           void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_dtype(dy_dtype)) return fail(FP8MI_ERR_ENUM, "dy_dtype %d is not F32/F16/BF16", dy_dtype);
   if (dy_dtype == FP8MI_F32) return fail(FP8MI_ERR_UNSUPPORTED, "fp8_bias_grad takes bf16 or fp16 gradients");
   if (rows < 0 || cols < 0) return fail(FP8MI_ERR_SHAPE, "negative shape rows=%lld cols=%lld", (long long)rows,
@@ -180,8 +184,15 @@ fp8mi_status fp8_bias_grad(const void* dy, int dy_dtype, int64_t rows, int64_t c
   if (rows > 0 && ld < cols) return fail(FP8MI_ERR_SHAPE, "ld %lld < cols %lld", (long long)ld, (long long)cols);
   if ((reinterpret_cast<uintptr_t>(dy) & 1u) || (reinterpret_cast<uintptr_t>(out) & 1u))
     return fail(FP8MI_ERR_ARG, "dy and out must be 2-byte aligned");
-  if ((cols + 63) / 64 > 0x7FFFFFFF) return fail(FP8MI_ERR_UNSUPPORTED, "cols beyond the launch grid");
-  return from_hip(launch_grad_bias(dy, dy_dtype, rows, cols, ld, static_cast<uint16_t*>(out),
+  const size_t need = (size_t)fp8mi::grad_bias_workspace_bytes(rows, cols);
+  if (need > 0 && !workspace) return fail(FP8MI_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(FP8MI_ERR_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(FP8MI_ERR_ARG, "workspace must be 8-byte aligned");
+  if ((cols + 511) / 512 > 0x7FFFFFFF || (rows + 127) / 128 > 65535)
+    return fail(FP8MI_ERR_UNSUPPORTED, "rows=%lld cols=%lld beyond the launch grid", (long long)rows,
+                (long long)cols);
+  return from_hip(launch_grad_bias(dy, dy_dtype, rows, cols, ld, static_cast<uint16_t*>(out), workspace,
                                    static_cast<hipStream_t>(stream)),
                   "bias grad launch");
 }

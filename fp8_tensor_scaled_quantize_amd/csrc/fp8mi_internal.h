@@ -34,8 +34,10 @@ struct MmArgs {
 
 hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 
+// Bytes of fp64 workspace the bias gradient needs (per-chunk column sums).
+int64_t grad_bias_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_grad_bias(const void* dy, int dt, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
-                            hipStream_t st);
+                            void* workspace, hipStream_t st);
 hipError_t launch_ring_seed(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st);
 
 }  // namespace fp8mi

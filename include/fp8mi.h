@@ -47,6 +47,7 @@
 #ifndef FP8MI_H
 #define FP8MI_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -165,13 +166,26 @@ FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t 
  * accumulated in fp64 in a fixed order and rounded once to bf16
  * (log:tests/extension, the commit reducing grad_b over leading dims; the
  * commit forcing gradients to bf16).
- *   dy   device, element (i, j) at dy[i * ld + j], dy_dtype FP8MI_BF16 or
- *        FP8MI_F16 (FP8MI_F32 returns FP8MI_ERR_UNSUPPORTED); ld >= cols.
- *   out  device bf16 [cols].
- * rows == 0 writes zeros; cols == 0 is a no-op.
+ *   dy         device, element (i, j) at dy[i * ld + j], dy_dtype FP8MI_BF16
+ *              or FP8MI_F16 (FP8MI_F32 returns FP8MI_ERR_UNSUPPORTED);
+ *              ld >= cols.
+ *   out        device bf16 [cols].
+ *   workspace  device scratch owned by the caller, 8-byte aligned, at least
+ *              fp8_bias_grad_workspace_bytes(rows, cols) bytes (NULL allowed
+ *              when that is 0).  Its contents are overwritten and need no
+ *              initialisation; calls in flight on the same workspace race.
+ * rows == 0 writes zeros; cols == 0 is a no-op.  A workspace that is missing
+ * or too small returns FP8MI_ERR_NULL / FP8MI_ERR_ARG before any launch.
  */
 FP8MI_API fp8mi_status fp8_bias_grad(const void* dy, int dy_dtype, int64_t rows, int64_t cols, int64_t ld,
-                                     void* out, void* stream);
+                                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_bias_grad_workspace_bytes -- device workspace fp8_bias_grad needs for a
+ * [rows, cols] gradient (per-chunk fp64 column sums); 0 when rows or cols is
+ * not positive.  Pure host function.
+ */
+FP8MI_API size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
  * fp8_ring_seed -- (re)initialise a ring on the device: history, ticket and

@@ -118,16 +118,28 @@ def test_binding_raises_without_gpu_on_bad_args():
         fp8mi.fp8_quantize(x, "e9m9", scale=None)
 
 
+def test_bias_grad_workspace_bytes(L):
+    f = L.fp8_bias_grad_workspace_bytes
+    assert f(0, 16) == 0 and f(16, 0) == 0 and f(-1, 4) == 0
+    assert f(1, 7) == 7 * 8                                 # one chunk of fp64 column sums
+    assert f(128, 7) == 7 * 8 and f(129, 7) == 2 * 7 * 8    # 128-row chunks
+    assert f(8192, 6912) == 64 * 6912 * 8
+
+
 def test_bias_grad_rejects(L):
     f = L.fp8_bias_grad
-    assert f(FAKE, 0, 4, 4, 4, FAKE, None) == UNSUP          # fp32 gradient
-    assert f(FAKE, 9, 4, 4, 4, FAKE, None) == ENUM
-    assert f(FAKE, 2, -1, 4, 4, FAKE, None) == SHAPE
-    assert f(FAKE, 2, 4, 4, 3, FAKE, None) == SHAPE
-    assert f(None, 2, 4, 4, 4, FAKE, None) == NULL
-    assert f(FAKE, 2, 4, 4, 4, None, None) == NULL
-    assert f(FAKE + 1, 2, 4, 4, 4, FAKE, None) == ARG
-    assert f(None, 2, 4, 0, 4, None, None) == OK            # no columns: no-op
+    W = L.fp8_bias_grad_workspace_bytes(4, 4)
+    assert f(FAKE, 0, 4, 4, 4, FAKE, FAKE, W, None) == UNSUP          # fp32 gradient
+    assert f(FAKE, 9, 4, 4, 4, FAKE, FAKE, W, None) == ENUM
+    assert f(FAKE, 2, -1, 4, 4, FAKE, FAKE, W, None) == SHAPE
+    assert f(FAKE, 2, 4, 4, 3, FAKE, FAKE, W, None) == SHAPE
+    assert f(None, 2, 4, 4, 4, FAKE, FAKE, W, None) == NULL
+    assert f(FAKE, 2, 4, 4, 4, None, FAKE, W, None) == NULL
+    assert f(FAKE + 1, 2, 4, 4, 4, FAKE, FAKE, W, None) == ARG
+    assert f(FAKE, 2, 4, 4, 4, FAKE, None, W, None) == NULL          # workspace missing
+    assert f(FAKE, 2, 4, 4, 4, FAKE, FAKE, W - 1, None) == ARG       # workspace too small
+    assert f(FAKE, 2, 4, 4, 4, FAKE, FAKE + 4, W, None) == ARG       # workspace misaligned
+    assert f(None, 2, 4, 0, 4, None, None, 0, None) == OK            # no columns: no-op
 
 
 def test_ring_seed_rejects(L):

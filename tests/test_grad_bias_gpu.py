@@ -35,6 +35,21 @@ def test_bias_grad_f16_and_strided():
     assert np.array_equal(np_bf16_bits(db), O.bf16_bits_from_f64(v))
 
 
+def test_bias_grad_caller_workspace_reused_and_checked():
+    # one caller-owned workspace (filled with garbage) serves two shapes in a row;
+    # 300 rows = 3 row chunks (the last ragged), 1100 columns = 3 column blocks (ragged)
+    ws = torch.full((fp8mi.fp8_bias_grad_workspace_bytes(300, 1100) // 8,), float("nan"), dtype=torch.float64,
+                    device=DEV)
+    for shape, seed in (((300, 1100), 82), ((129, 700), 83)):
+        dy = synth.gaussian(shape, 1e-3, "bf16", seed, 0)
+        db = fp8mi.fp8_bias_grad(to_device(dy, "bf16"), workspace=ws)
+        ref, mag = O.grad_bias(dy)
+        assert np.array_equal(np_bf16_bits(db), ref), shape
+    small = torch.empty(fp8mi.fp8_bias_grad_workspace_bytes(300, 1100) - 8, dtype=torch.uint8, device=DEV)
+    with pytest.raises(fp8mi.Fp8Error):
+        fp8mi.fp8_bias_grad(to_device(synth.gaussian((300, 1100), 1e-3, "bf16", 84, 0), "bf16"), workspace=small)
+
+
 def test_bias_grad_zero_rows():
     db = fp8mi.fp8_bias_grad(torch.empty((0, 33), dtype=torch.bfloat16, device=DEV))
     assert torch.all(db == 0)
