@@ -354,11 +354,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
       }
     }
     __syncthreads();
-    // BN / 8 lanes x 16 bytes per row; a wave stores 64 / (BN / 8) rows per step.
+    // BN / 8 lanes x 16 bytes per row; a wave stores RPW rows per step (lanes
+    // past RPW * LPR idle when BN / 8 does not divide 64, e.g. BN = 192)
     constexpr int LPR = BN / 8, RPW = 64 / LPR;
     const int sub = lane / LPR, cl = lane % LPR;
 #pragma unroll 4
-    for (int rr = wid * RPW + sub; rr < BM; rr += RPW * NWAVES) {
+    for (int rr = wid * RPW + sub; sub < RPW && rr < BM; rr += RPW * NWAVES) {
       const uint4 v = *reinterpret_cast<const uint4*>(Cs + rr * CROW + 8 * cl);
       *reinterpret_cast<uint4*>(C + (m0 + rr) * p.ldc + n0 + 8 * cl) = v;
     }
@@ -388,12 +389,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 }
 
 // Tile dispatch (measured on MI355X over the shapes of the test configs):
-// the 256x256 / 8-wave kernel whenever its tiles (x batch) cover at least 60%
-// of the CUs -- one round of big tiles beats several rounds of small ones even
-// with a quarter of the CUs idle -- and the 64x128 / 4-wave kernel (two per
-// CU) below that, where it beat 128x128 on every shape measured.  128x128 is
-// reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128 kernel
-// remains for operands whose byte extent does not fit a 32-bit buffer offset.
+// the 8-wave big-tile kernels whenever their tiles (x batch) cover at least
+// 60% of the CUs -- one round of big tiles beats several rounds of small ones
+// even with part of the chip idle -- choosing 256 x 192 over 256 x 256 when it
+// needs less work per CU (rounds of workgroups x tile width: the backward
+// GEMMs of the 1536-wide linear get 256 and 216 workgroups instead of 192 and
+// 162, 10-11% faster), and the 64x128 / 4-wave kernel (two per CU) below 60%.
+// 128x128 is reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128
+// kernel remains for operands whose byte extent does not fit a 32-bit buffer
+// offset.
 template <int FA, int FB, int BM, int BN, int WM_, int WN_, int MINB>
 static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
   const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -405,9 +409,13 @@ static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
 
 static int pick_tile(const MmArgs& p, int ncu) {
   static const int forced = [] { const char* e = getenv("FP8MI_MM_TILE"); return e ? atoi(e) : -1; }();
-  if (forced >= 0 && forced < 3) return forced;
-  const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-  return 10 * t256 >= 6 * (int64_t)ncu ? 0 : 2;
+  if (forced >= 0 && forced < 4) return forced;
+  const int64_t tm = (p.M + 255) / 256;
+  const int64_t t256 = tm * ((p.N + 255) / 256) * p.batch, t192 = tm * ((p.N + 191) / 192) * p.batch;
+  if (10 * (t256 > t192 ? t256 : t192) < 6 * (int64_t)ncu) return 2;
+  // per-CU work of the big-tile family: rounds of workgroups x tile width
+  const int64_t cost256 = ((t256 + ncu - 1) / ncu) * 256, cost192 = ((t192 + ncu - 1) / ncu) * 192;
+  return cost192 < cost256 ? 3 : 0;
 }
 
 template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStream_t st) {
@@ -416,6 +424,7 @@ template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStre
   if (fits31) {
     switch (pick_tile(p, device_cu_count())) {
       case 0: return launch_dma<FA, FB, 256, 256, 2, 4, 1>(p, st);
+      case 3: return launch_dma<FA, FB, 256, 192, 2, 4, 1>(p, st);
       case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2>(p, st);
       default: return launch_dma<FA, FB, 64, 128, 1, 4, 2>(p, st);
     }
