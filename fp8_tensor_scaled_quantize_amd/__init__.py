@@ -13,7 +13,7 @@ import torch
 
 from ._lib import lib
 
-__all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual",
+__all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual", "fp8_quantize_dual_bias_grad",
            "fp8_amax_fold", "fp8_mm", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
 
 E4M3, E5M2 = 0, 1
@@ -142,6 +142,38 @@ def fp8_quantize_dual(x: torch.Tensor, fmt, out_row: torch.Tensor | None = None,
     _check(lib().fp8_quantize_dual(_ptr(x), _DT[x.dtype], rows, cols, ld_x, f, _ptr(out_row), ld_r, _ptr(out_t),
                                    ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out), _ptr(amax_out), _stream(x)))
     return out_row, out_t
+
+
+def fp8_quantize_dual_bias_grad(dy: torch.Tensor, fmt, out_row: torch.Tensor | None = None,
+                                out_t: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                                ring: torch.Tensor | None = None, scale_inv_out: torch.Tensor | None = None,
+                                amax_out: torch.Tensor | None = None, bias_grad_out: torch.Tensor | None = None,
+                                workspace: torch.Tensor | None = None):
+    """fp8_quantize_dual of a 2-D bf16/fp16 gradient plus its bias gradient
+    from the same read; returns (codes, codes_t, bias_grad bf16 [cols])."""
+    if dy.dim() != 2 or (dy.shape[1] > 1 and dy.stride(1) != 1):
+        raise ValueError("dy must be 2-D with unit column stride")
+    rows, cols = dy.shape
+    f = _fmt(fmt)
+    if out_row is None:
+        out_row = torch.empty((rows, cols), dtype=torch.uint8, device=dy.device)
+    if out_t is None:
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=dy.device)
+    if bias_grad_out is None:
+        bias_grad_out = torch.empty(cols, dtype=torch.bfloat16, device=dy.device)
+    need = fp8_bias_grad_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dy.device)
+    out_row, out_t = _as_codes(out_row), _as_codes(out_t)
+    ld_x = dy.stride(0) if rows > 1 else cols
+    ld_r = out_row.stride(0) if out_row.shape[0] > 1 else out_row.shape[1]
+    ld_t = out_t.stride(0) if out_t.shape[0] > 1 else out_t.shape[1]
+    rp, h = _ring_args(ring)
+    _check(lib().fp8_quantize_dual_bias_grad(_ptr(dy), _DT[dy.dtype], rows, cols, ld_x, f, _ptr(out_row), ld_r,
+                                             _ptr(out_t), ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out),
+                                             _ptr(amax_out), _ptr(bias_grad_out), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(dy)))
+    return out_row, out_t, bias_grad_out
 
 
 def fp8_amax_fold(ring: torch.Tensor, amax: torch.Tensor, fmt) -> None:

@@ -70,7 +70,7 @@ static fp8mi_status check_input(const void* x, int dt, int64_t rows, int64_t col
 static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
                                     int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
                                     const float* scale, uint32_t* ring, int32_t H, float* scale_inv_out,
-                                    float* amax_out, void* stream) {
+                                    float* amax_out, void* stream, double* bias_ws = nullptr) {
   fp8mi_status s = check_input(x, dt, rows, cols, ld_x);
   if (s != FP8MI_OK) return s;
   if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
@@ -91,8 +91,25 @@ static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t
       reinterpret_cast<uintptr_t>(amax_out) & 3u)
     return fail(FP8MI_ERR_ARG, "fp32 scalars must be 4-byte aligned");
   hipError_t e = launch_quantize(x, dt, rows, cols, ld_x, fmt, mode, out_row, ld_row, out_t, ld_t, scale, ring, H,
-                                 scale_inv_out, amax_out, static_cast<hipStream_t>(stream));
+                                 scale_inv_out, amax_out, static_cast<hipStream_t>(stream), bias_ws);
   return from_hip(e, "quantize launch");
+}
+
+// Bias-gradient arguments shared by fp8_bias_grad and the fused dual quantize.
+static fp8mi_status check_bias_grad(int dt, int64_t rows, int64_t cols, const void* out, const void* workspace,
+                                    size_t workspace_bytes) {
+  if (dt == FP8MI_F32) return fail(FP8MI_ERR_UNSUPPORTED, "the bias gradient takes bf16 or fp16 gradients");
+  if (cols > 0 && !out) return fail(FP8MI_ERR_NULL, "bias gradient output is NULL");
+  if (reinterpret_cast<uintptr_t>(out) & 1u) return fail(FP8MI_ERR_ARG, "bias gradient output must be 2-byte aligned");
+  const size_t need = (size_t)grad_bias_workspace_bytes(rows, cols);
+  if (need > 0 && !workspace) return fail(FP8MI_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(FP8MI_ERR_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(FP8MI_ERR_ARG, "workspace must be 8-byte aligned");
+  if ((cols + 511) / 512 > 0x7FFFFFFF || (rows + 127) / 128 > 65535)
+    return fail(FP8MI_ERR_UNSUPPORTED, "rows=%lld cols=%lld beyond the launch grid", (long long)rows,
+                (long long)cols);
+  return FP8MI_OK;
 }
 
 }  // namespace fp8mi
@@ -118,6 +135,22 @@ fp8mi_status fp8_quantize_dual(const void* x, int x_dtype, int64_t rows, int64_t
                                void* stream) {
   return quantize_common(x, x_dtype, rows, cols, ld_x, fmt, 2, out_row, ld_row, out_t, ld_t, scale, ring, hist_len,
                          scale_inv_out, amax_out, stream);
+}
+
+fp8mi_status fp8_quantize_dual_bias_grad(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                         int fmt, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
+                                         const float* scale, uint32_t* ring, int32_t hist_len, float* scale_inv_out,
+                                         float* amax_out, void* bias_grad_out, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(x_dtype)) return fail(FP8MI_ERR_ENUM, "x_dtype %d is not F32/F16/BF16", x_dtype);
+  fp8mi_status s = check_bias_grad(x_dtype, rows, cols, bias_grad_out, workspace, workspace_bytes);
+  if (s != FP8MI_OK) return s;
+  s = quantize_common(x, x_dtype, rows, cols, ld_x, fmt, 2, out_row, ld_row, out_t, ld_t, scale, ring, hist_len,
+                      scale_inv_out, amax_out, stream, static_cast<double*>(workspace));
+  if (s != FP8MI_OK || cols == 0) return s;
+  return from_hip(launch_grad_bias_finalize(static_cast<const double*>(workspace), rows, cols,
+                                            static_cast<uint16_t*>(bias_grad_out), static_cast<hipStream_t>(stream)),
+                  "bias grad finalize launch");
 }
 
 fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const float* amax, int fmt, void* stream) {
@@ -182,16 +215,9 @@ fp8mi_status fp8_bias_grad(const void* dy, int dy_dtype, int64_t rows, int64_t c
   if (!out) return fail(FP8MI_ERR_NULL, "out is NULL");
   if (rows > 0 && !dy) return fail(FP8MI_ERR_NULL, "dy is NULL");
   if (rows > 0 && ld < cols) return fail(FP8MI_ERR_SHAPE, "ld %lld < cols %lld", (long long)ld, (long long)cols);
-  if ((reinterpret_cast<uintptr_t>(dy) & 1u) || (reinterpret_cast<uintptr_t>(out) & 1u))
-    return fail(FP8MI_ERR_ARG, "dy and out must be 2-byte aligned");
-  const size_t need = (size_t)fp8mi::grad_bias_workspace_bytes(rows, cols);
-  if (need > 0 && !workspace) return fail(FP8MI_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
-  if (workspace_bytes < need)
-    return fail(FP8MI_ERR_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(FP8MI_ERR_ARG, "workspace must be 8-byte aligned");
-  if ((cols + 511) / 512 > 0x7FFFFFFF || (rows + 127) / 128 > 65535)
-    return fail(FP8MI_ERR_UNSUPPORTED, "rows=%lld cols=%lld beyond the launch grid", (long long)rows,
-                (long long)cols);
+  if (reinterpret_cast<uintptr_t>(dy) & 1u) return fail(FP8MI_ERR_ARG, "dy must be 2-byte aligned");
+  fp8mi_status s = check_bias_grad(dy_dtype, rows, cols, out, workspace, workspace_bytes);
+  if (s != FP8MI_OK) return s;
   return from_hip(launch_grad_bias(dy, dy_dtype, rows, cols, ld, static_cast<uint16_t*>(out), workspace,
                                    static_cast<hipStream_t>(stream)),
                   "bias grad launch");

@@ -8,10 +8,13 @@ namespace fp8mi {
 // Compute-unit count of the current device (cached per device).
 int device_cu_count();
 
-// mode: 0 row, 1 transposed, 2 dual.  Arguments already validated.
+// mode: 0 row, 1 transposed, 2 dual.  Arguments already validated.  With
+// bias_ws (dual, bf16/fp16 input) the dual kernel also writes fp64 column sums
+// per 128-row tile to bias_ws[tile row][col] (the grad_bias workspace layout).
 hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt, int mode,
                            uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t, const float* scale,
-                           uint32_t* ring, int H, float* scale_inv_out, float* amax_out, hipStream_t st);
+                           uint32_t* ring, int H, float* scale_inv_out, float* amax_out, hipStream_t st,
+                           double* bias_ws = nullptr);
 
 hipError_t launch_amax_fold(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st);
 
@@ -38,6 +41,8 @@ hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 int64_t grad_bias_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_grad_bias(const void* dy, int dt, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
                             void* workspace, hipStream_t st);
+// Second half of the bias gradient: adds the per-chunk sums in chunk order, one bf16 rounding.
+hipError_t launch_grad_bias_finalize(const double* ws, int64_t rows, int64_t cols, uint16_t* out, hipStream_t st);
 hipError_t launch_ring_seed(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st);
 
 }  // namespace fp8mi

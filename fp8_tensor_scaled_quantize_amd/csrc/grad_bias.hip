@@ -143,6 +143,11 @@ hipError_t launch_grad_bias(const void* dy, int dt, int64_t rows, int64_t cols, 
     else
       hipLaunchKernelGGL((grad_bias_partials<kBF16>), grid, dim3(kGbThreads), 0, st, dy, rows, cols, ld, ws);
   }
+  return launch_grad_bias_finalize(ws, rows, cols, out, st);
+}
+
+hipError_t launch_grad_bias_finalize(const double* ws, int64_t rows, int64_t cols, uint16_t* out, hipStream_t st) {
+  const int64_t nchunk = rows > 0 ? (rows + kGbRowChunk - 1) / kGbRowChunk : 0;
   hipLaunchKernelGGL(grad_bias_finalize, dim3((unsigned)((cols + kGbFinCols - 1) / kGbFinCols)),
                      dim3(kGbFinCols * kGbFinSplit), 0, st, ws, nchunk, cols, out);
   return hipGetLastError();

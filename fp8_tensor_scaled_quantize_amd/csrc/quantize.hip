@@ -42,6 +42,7 @@ struct QuantArgs {
   int H;
   float* scale_inv_out;
   float* amax_out;
+  double* bias_ws;      // dual with bias gradient: fp64 column sums per 128-row tile, [tile row][col]
 };
 
 // Shared ending of every quantize workgroup.
@@ -262,11 +263,12 @@ __device__ __forceinline__ int lds_t_index(int c, int w) { return c * 32 + (w ^ 
 
 // One-shot form: each workgroup loads, encodes and stores its tiles in turn
 // (launched with one tile per workgroup; low registers, high occupancy).
-template <int DT, int FMT, int MODE>
+template <int DT, int FMT, int MODE, bool BG = false>
 __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int64_t tiles_c, int64_t ntiles,
                                                                 int64_t tiles_per_block) {
   __shared__ float red[kTileThreads / 64];
   __shared__ __align__(16) uint32_t lds_t[(MODE == kRow) ? 1 : kTileC * 32];
+  __shared__ double bg_red[BG ? kTileThreads / 64 : 1][BG ? kTileC : 1];
   constexpr int EB = In<DT>::kBytes;
   const float s = read_scale<FMT>(p);
   const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
@@ -363,7 +365,35 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
                              (((rw[2][h] >> sh) & 0xFFu) << 16) | (((rw[3][h] >> sh) & 0xFFu) << 24);
         lds_t[lds_t_index(8 * cg + e, rg)] = col;
       }
+      if constexpr (BG) {
+        // bias gradient: fp64 column sums of the raw values -- this thread's 4
+        // rows in order, the wave's 8 row groups by xor butterfly, then (after
+        // the barrier) the 4 waves in order
+        double cs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          double v = (double)f[0][e];
+#pragma unroll
+          for (int i = 1; i < 4; ++i) v += (double)f[i][e];
+          v += __shfl_xor(v, 8, 64);
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          cs[e] = v;
+        }
+        if ((t & 63) < 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bg_red[t >> 6][8 * cg + e] = cs[e];
+        }
+      }
       __syncthreads();
+      if constexpr (BG) {
+        if (t < kTileC && c0 + t < p.cols) {
+          double v = bg_red[0][t];
+#pragma unroll
+          for (int w = 1; w < kTileThreads / 64; ++w) v += bg_red[w][t];
+          p.bias_ws[(r0 / kTileR) * p.cols + c0 + t] = v;
+        }
+      }
       // 64 transposed rows (one per input column) x 128 bytes; lane: row cl, 16 bytes at 16q
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
@@ -399,11 +429,12 @@ template <int DT> struct TileRaw {
   uint32_t full;  // bit i: row i came through vector loads
 };
 
-template <int DT, int FMT, int MODE>
+template <int DT, int FMT, int MODE, bool BG = false>
 __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, int64_t tiles_c, int64_t ntiles,
                                                                 int64_t tiles_per_block) {
   __shared__ float red[kTileThreads / 64];
   __shared__ __align__(16) uint32_t lds_t[(MODE == kRow) ? 1 : kTileC * 32];
+  __shared__ double bg_red[BG ? kTileThreads / 64 : 1][BG ? kTileC : 1];
   constexpr int EB = In<DT>::kBytes;
   constexpr int NLD = TileRaw<DT>::kLoads;
   const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
@@ -514,7 +545,35 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
                              (((rw[2][h] >> sh) & 0xFFu) << 16) | (((rw[3][h] >> sh) & 0xFFu) << 24);
         lds_t[lds_t_index(8 * cg + e, rg)] = col;
       }
+      if constexpr (BG) {
+        // bias gradient: fp64 column sums of the raw values -- this thread's 4
+        // rows in order, the wave's 8 row groups by xor butterfly, then (after
+        // the barrier) the 4 waves in order
+        double cs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          double v = (double)f[0][e];
+#pragma unroll
+          for (int i = 1; i < 4; ++i) v += (double)f[i][e];
+          v += __shfl_xor(v, 8, 64);
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          cs[e] = v;
+        }
+        if ((t & 63) < 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bg_red[t >> 6][8 * cg + e] = cs[e];
+        }
+      }
       __syncthreads();
+      if constexpr (BG) {
+        if (t < kTileC && c0 + t < p.cols) {
+          double v = bg_red[0][t];
+#pragma unroll
+          for (int w = 1; w < kTileThreads / 64; ++w) v += bg_red[w][t];
+          p.bias_ws[(r0 / kTileR) * p.cols + c0 + t] = v;
+        }
+      }
       // 64 transposed rows (one per input column) x 128 bytes; lane: row cl, 16 bytes at 16q
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
@@ -579,13 +638,14 @@ static int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-template <int DT, int FMT, int M>
+template <int DT, int FMT, int M, bool BG = false>
 static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantArgs& p, int64_t tiles_c,
                          int64_t ntiles, int64_t tpb) {
   if (one_shot) {
-    hipLaunchKernelGGL((quantize_tiled<DT, FMT, M>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
+    hipLaunchKernelGGL((quantize_tiled<DT, FMT, M, BG>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
   } else {
-    hipLaunchKernelGGL((quantize_tiled_pf<DT, FMT, M>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
+    hipLaunchKernelGGL((quantize_tiled_pf<DT, FMT, M, BG>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles,
+                       tpb);
   }
 }
 
@@ -618,7 +678,15 @@ static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   switch (mode) {
     case kRow: launch_tiled<DT, FMT, kRow>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
     case kTrans: launch_tiled<DT, FMT, kTrans>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
-    default: launch_tiled<DT, FMT, kDual>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
+    default:
+      if constexpr (DT != kF32) {
+        if (p.bias_ws) {
+          launch_tiled<DT, FMT, kDual, true>(one_shot, grid, st, p, tiles_c, ntiles, tpb);
+          break;
+        }
+      }
+      launch_tiled<DT, FMT, kDual>(one_shot, grid, st, p, tiles_c, ntiles, tpb);
+      break;
   }
   return hipGetLastError();
 }
@@ -633,8 +701,9 @@ template <int FMT> static hipError_t launch_fmt(const QuantArgs& p, int dt, int 
 
 hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt, int mode,
                            uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t, const float* scale,
-                           uint32_t* ring, int H, float* scale_inv_out, float* amax_out, hipStream_t st) {
-  QuantArgs p{x, rows, cols, ld_x, out_row, ld_row, out_t, ld_t, scale, ring, H, scale_inv_out, amax_out};
+                           uint32_t* ring, int H, float* scale_inv_out, float* amax_out, hipStream_t st,
+                           double* bias_ws) {
+  QuantArgs p{x, rows, cols, ld_x, out_row, ld_row, out_t, ld_t, scale, ring, H, scale_inv_out, amax_out, bias_ws};
   if (!ring && amax_out) {
     hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, st, amax_out);
     hipError_t e = hipGetLastError();

@@ -13,7 +13,8 @@ backward(dY): dY -> E5M2 codes in both layouts with ring g (fp8_quantize_dual)
               dX = Gq (Wq^T)^T * sg_inv * sw_inv            (fp8_mm, NT on W^T codes)
               dW = Gq^T (Xq^T)^T * sg_inv * sx_inv          (fp8_mm, NT on the
                                                             transposed codes)
-              db = sum of dY over leading dims              (fp8_bias_grad)
+              db = sum of dY over leading dims              (fused into dY's dual
+                                                            quantize: fp8_quantize_dual_bias_grad)
 
 The scale_inv values a quantize writes are the snapshot of the scale it used,
 taken before its fold publishes the next one, and backward reuses the
@@ -27,7 +28,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (E4M3, E5M2, fp8_bias_grad, fp8_mm, fp8_quantize, fp8_quantize_dual, fp8_ring_seed,
+from . import (E4M3, E5M2, fp8_mm, fp8_quantize, fp8_quantize_dual, fp8_quantize_dual_bias_grad, fp8_ring_seed,
                new_ring)
 
 
@@ -87,9 +88,12 @@ class Fp8Linear:
         N = self.weight.shape[0]
         dy2 = dy.reshape(-1, N)
         sx, sw, sg = self.scale_inv[0:1], self.scale_inv[1:2], self.scale_inv[2:3]
-        gq, gq_t = fp8_quantize_dual(dy2, E5M2, ring=self.ring_g, scale_inv_out=sg)
+        if self.bias is not None:  # the bias gradient comes from the quantize's own read of dY
+            gq, gq_t, db = fp8_quantize_dual_bias_grad(dy2, E5M2, ring=self.ring_g, scale_inv_out=sg)
+        else:
+            gq, gq_t = fp8_quantize_dual(dy2, E5M2, ring=self.ring_g, scale_inv_out=sg)
+            db = None
         dx = fp8_mm(gq, wq_t, E5M2, E4M3, sg, sw)
         dw = fp8_mm(gq_t, xq_t, E5M2, E4M3, sg, sx)
-        db = fp8_bias_grad(dy2) if self.bias is not None else None
         self.last_grad_codes = (gq, gq_t)
         return dx.reshape(x_shape), dw, db

@@ -161,6 +161,30 @@ FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t 
                     void* c, int64_t ldc, int64_t stride_c, void* stream);
 
 /*
+ * fp8_quantize_dual_bias_grad -- fp8_quantize_dual of an output gradient
+ * plus its bias gradient from the same read: the codes, scale_inv and ring
+ * update are exactly those of fp8_quantize_dual, and bias_grad_out[j] is the
+ * sum of the raw dy[i, j] over all rows (the pages reduce grad_b over the
+ * leading dimensions of the gradient before any quantization:
+ * log:tests/extension, the commit fixing the 3-D backward and the commit
+ * forcing gradients to bf16), accumulated in fp64 in a fixed order and
+ * rounded once to bf16 -- within rounding of fp8_bias_grad, whose summation
+ * order differs.
+ *   x            the gradient, FP8MI_BF16 or FP8MI_F16 (FP8MI_F32 returns
+ *                FP8MI_ERR_UNSUPPORTED); other arguments as fp8_quantize_dual.
+ *   bias_grad_out  device bf16 [cols].
+ *   workspace    as fp8_bias_grad: fp8_bias_grad_workspace_bytes(rows, cols)
+ *                bytes, 8-byte aligned, caller-owned, no initialisation.
+ * Two launches (the dual quantize, then a small finalize) on `stream`.
+ */
+FP8MI_API fp8mi_status fp8_quantize_dual_bias_grad(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                                   int64_t ld_x, int fmt, uint8_t* out_row, int64_t ld_row,
+                                                   uint8_t* out_t, int64_t ld_t, const float* scale, uint32_t* ring,
+                                                   int32_t hist_len, float* scale_inv_out, float* amax_out,
+                                                   void* bias_grad_out, void* workspace, size_t workspace_bytes,
+                                                   void* stream);
+
+/*
  * fp8_bias_grad -- bias gradient of an fp8 linear layer: out[j] = the sum of
  * dy[i, j] over all rows i (every leading dimension flattened into rows),
  * accumulated in fp64 in a fixed order and rounded once to bf16

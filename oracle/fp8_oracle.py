@@ -340,12 +340,12 @@ def within_tolerance(gpu_bits, ref_bits, abs_sum, rel=1e-5):
     return ok | ((g == r) & ~np.isnan(g))
 
 
-def grad_bias(dy_bits: np.ndarray):
-    """Bias gradient: sum of the bf16 upstream gradient over every leading
-    dimension, summed in float64 and rounded once to bf16 (log:tests/extension,
-    the commit reducing grad_b over leading dims; grads are bf16).
-    Returns (bits, abs_sum) for the same tolerance form as the GEMM."""
-    v = widen_to_f32(dy_bits, BF16).astype(np.float64)
+def grad_bias(dy_bits: np.ndarray, dtype: str = BF16):
+    """Bias gradient: sum of the bf16 (or fp16) upstream gradient over every
+    leading dimension, summed in float64 and rounded once to bf16
+    (log:tests/extension, the commit reducing grad_b over leading dims; grads
+    are bf16).  Returns (bits, abs_sum) for the same tolerance form as the GEMM."""
+    v = widen_to_f32(dy_bits, dtype).astype(np.float64)
     v = v.reshape(-1, v.shape[-1])
     return bf16_bits_from_f64(v.sum(axis=0)), np.abs(v).sum(axis=0)
 

@@ -142,6 +142,26 @@ def test_bias_grad_rejects(L):
     assert f(None, 2, 4, 0, 4, None, None, 0, None) == OK            # no columns: no-op
 
 
+def test_fused_dual_bias_grad_rejects(L):
+    f = L.fp8_quantize_dual_bias_grad
+    W = L.fp8_bias_grad_workspace_bytes(4, 4)
+    ring, H = FAKE, 4
+
+    def call(x=FAKE, dt=2, rows=4, cols=4, ld=4, fmt=0, o_row=FAKE, o_t=FAKE, scale=None, ring=ring, h=H,
+             db=FAKE, ws=FAKE, wsb=W):
+        return f(x, dt, rows, cols, ld, fmt, o_row, 4, o_t, 4, scale, ring, h, None, None, db, ws, wsb, None)
+
+    assert call(dt=0) == UNSUP          # fp32 gradient
+    assert call(dt=9) == ENUM
+    assert call(db=None) == NULL        # bias gradient output missing
+    assert call(ws=None) == NULL        # workspace missing
+    assert call(wsb=W - 1) == ARG       # workspace too small
+    assert call(db=FAKE + 1) == ARG     # misaligned bias gradient output
+    assert call(fmt=5) == ENUM          # then the dual quantize's own checks
+    assert call(o_t=None) == NULL
+    assert call(rows=-1) == SHAPE
+
+
 def test_ring_seed_rejects(L):
     f = L.fp8_ring_seed
     assert f(None, 4, FAKE, 0, None) == NULL
