@@ -182,7 +182,8 @@ def next_scale(hist: np.ndarray, fmt: str) -> np.float32:
     m = np.float32(np.max(np.asarray(hist, dtype=np.float32)))
     if not (np.isfinite(m) and m > 0):
         return np.float32(1.0)
-    s = np.float32(FMT_MAX[fmt]) / m
+    with np.errstate(over="ignore"):
+        s = np.float32(FMT_MAX[fmt]) / m
     if not (np.isfinite(s) and s > 0):
         return np.float32(1.0)
     return np.float32(s)
@@ -252,6 +253,20 @@ def quantize(x: np.ndarray, dtype: str, fmt: str, scale=None, ring: Ring | None 
     new_ring = fold(ring, a, fmt) if ring is not None else None
     return {"codes": codes, "codes_t": np.ascontiguousarray(codes.T), "amax": a,
             "scale_inv": scale_inv(s), "ring": new_ring}
+
+
+def quantize_dynamic(x: np.ndarray, dtype: str, fmt: str):
+    """Current (dynamic) scaling: no history ring; the scale is measured from
+    the tensor being quantized and used by the same call (log:tests/extension,
+    the commit merging the delayed and dynamic recipes behind one `dynamic`
+    flag, and the commit skipping scale-meta allocation on the dynamic path,
+    whose scales are measured inline).  The pages give no formula of their own
+    for it; the reading taken is the delayed rule over a window that holds
+    only this tensor's amax: s = fmt_max / amax(x), 1.0 when amax is 0 or not
+    finite or the quotient is not a finite positive number.  Returns the same
+    dict as quantize (ring None)."""
+    s = next_scale(np.array([amax(widen_to_f32(x, dtype))], dtype=np.float32), fmt)
+    return quantize(x, dtype, fmt, scale=s)
 
 
 # --------------------------------------------------------------------------

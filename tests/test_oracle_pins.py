@@ -473,3 +473,81 @@ def test_linear_backward_shapes_and_transposes():
     assert np.allclose(dx, G @ W, rtol=1e-2, atol=1e-9)
     assert np.allclose(dw, G.T @ X, rtol=1e-2, atol=1e-9)
     del g
+
+
+# ------------------------------------------------------- current scaling ----
+def _golden_input(vals, dtype):
+    f = np.array(vals, dtype=np.float32)
+    if dtype == O.BF16:
+        bits = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        assert np.array_equal(O.widen_to_f32(bits, dtype).view(np.uint32), f.view(np.uint32)), "not exact in bf16"
+        return bits
+    if dtype == O.F16:
+        h = f.astype(np.float16)
+        assert np.array_equal(h.astype(np.float32), f), "not exact in fp16"
+        return h
+    return f
+
+
+def test_dynamic_golden_worked():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "dynamic_worked.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        case, fmt, dtype, vals, sinv, am, codes = line.split()
+        x = _golden_input([float(v) for v in vals.split(",")], dtype)[None, :]
+        r = O.quantize_dynamic(x, dtype, fmt)
+        assert r["scale_inv"] == np.float32(float(sinv)), case
+        assert r["amax"] == np.float32(float(am)), case
+        assert r["codes"][0].tolist() == [int(c, 16) for c in codes.split(",")], case
+        assert r["ring"] is None
+        n += 1
+    assert n == 8
+
+
+@pytest.mark.parametrize("fmt,top", [(O.E4M3, 0x7E), (O.E5M2, 0x7B)])
+@pytest.mark.parametrize("dtype", O.DTYPES)
+def test_dynamic_scale_is_nearest_quotient_and_hits_format_max(fmt, top, dtype):
+    """The scale is the fp32 nearest of the exact quotient fmt_max / amax(x)
+    (checked with exact fractions), scale_inv its fp32 reciprocal, and the
+    element(s) of largest magnitude land on the format's largest code while
+    no code exceeds it."""
+    for seed, sigma in ((1, 1.0), (2, 3e-3), (3, 7e2)):
+        x = synth.gaussian((37, 29), sigma, dtype, 90, seed)
+        xf = O.widen_to_f32(x, dtype)
+        a = float(np.max(np.abs(xf)))
+        r = O.quantize_dynamic(x, dtype, fmt)
+        s = np.float32(float(Fraction(O.FMT_MAX[fmt]) / Fraction(a)))
+        assert r["amax"] == np.float32(a)
+        assert r["scale_inv"] == np.float32(float(Fraction(1) / Fraction(float(s))))
+        mag = r["codes"] & 0x7F
+        assert mag.max() == top
+        assert np.all(mag[np.abs(xf) == np.float32(a)] == top)
+        # the scaled tensor spans the format: the scale is not the reciprocal
+        # of the quotient, nor measured from anything but this tensor
+        assert np.array_equal(r["codes"], O.quantize(x, dtype, fmt, scale=s)["codes"])
+
+
+def test_dynamic_depends_on_this_tensor_only():
+    """Two tensors that differ by a power-of-two factor get the same codes;
+    a tensor with one element raised gets a smaller scale for all the rest."""
+    x = synth.gaussian((16, 24), 1.0, O.F32, 91, 0)
+    r1 = O.quantize_dynamic(x, O.F32, O.E4M3)
+    r2 = O.quantize_dynamic(x * np.float32(2.0 ** -20), O.F32, O.E4M3)
+    assert np.array_equal(r1["codes"], r2["codes"])
+    assert r2["scale_inv"] == r1["scale_inv"] * np.float32(2.0 ** -20)
+    y = x.copy()
+    y[3, 5] = np.float32(4 * np.max(np.abs(x)))
+    r3 = O.quantize_dynamic(y, O.F32, O.E4M3)
+    assert r3["scale_inv"] > r1["scale_inv"]
+    assert r3["codes"][3, 5] == 0x7E
+
+
+def test_dynamic_equals_delayed_with_a_ring_seeded_from_the_same_tensor():
+    for dtype in O.DTYPES:
+        x = synth.gaussian((19, 40), 0.5, dtype, 92, 1)
+        r = O.quantize_dynamic(x, dtype, O.E5M2)
+        d = O.quantize(x, dtype, O.E5M2, ring=O.seed_ring(4, x, dtype, O.E5M2))
+        assert np.array_equal(r["codes"], d["codes"])
+        assert r["scale_inv"] == d["scale_inv"] and r["amax"] == d["amax"]
