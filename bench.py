@@ -221,7 +221,9 @@ def main():
 
     total_ms = timed(lambda i: step(args.warmup + i), args.steps) * args.steps
     nlaunch = max(10, args.steps)
-    names = ["quantize_row", "quantize_transposed", "quantize_dual", "mm_fp8"]
+    names = ["quantize_row", "quantize_transposed", "quantize_dual", "mm_fp8", "quantize_dynamic_row",
+             "quantize_dynamic_dual"]
+    ws_dyn = torch.empty(fp8mi.DYNAMIC_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     launches = {
         "quantize_row": lambda i: fp8mi.fp8_quantize(xq[i % nq], fp8mi.E4M3, False, out=out_row, ring=rings[0],
                                                       scale_inv_out=sinv[0:1]),
@@ -230,16 +232,27 @@ def main():
         "quantize_dual": lambda i: fp8mi.fp8_quantize_dual(xq[i % nq], fp8mi.E4M3, out_row=out_row2, out_t=out_t2,
                                                            ring=rings[2], scale_inv_out=sinv[2:3]),
         "mm_fp8": lambda i: fp8mi.fp8_mm(A[i % nm], B[i % nm], fp8mi.E4M3, fp8mi.E4M3, sa, sb, bias, out=C_out),
+        # current scaling: amax pass + quantize pass per call
+        "quantize_dynamic_row": lambda i: fp8mi.fp8_quantize_dynamic(xq[i % nq], fp8mi.E4M3, 0, out_row=out_row,
+                                                                     scale_inv_out=sinv[0:1], workspace=ws_dyn),
+        "quantize_dynamic_dual": lambda i: fp8mi.fp8_quantize_dynamic(xq[i % nq], fp8mi.E4M3, 2, out_row=out_row2,
+                                                                      out_t=out_t2, scale_inv_out=sinv[2:3],
+                                                                      workspace=ws_dyn),
     }
     us = [timed(launches[nme], nlaunch) * 1e3 for nme in names]
-    qbytes = {"quantize_row": R * C * 3, "quantize_transposed": R * C * 3, "quantize_dual": R * C * 4}
+    qbytes = {"quantize_row": R * C * 3, "quantize_transposed": R * C * 3, "quantize_dual": R * C * 4,
+              "quantize_dynamic_row": R * C * 3, "quantize_dynamic_dual": R * C * 4}
     flops = 2.0 * M * N * K
     mm_tflops = flops / (us[3] * 1e-6) / 1e12
     quant = {}
-    for i, nme in enumerate(names[:3]):
+    for i, nme in enumerate(names):
+        if nme == "mm_fp8":
+            continue
         gbs = qbytes[nme] / (us[i] * 1e-6) / 1e9
         quant[nme] = {"us_per_launch": round(float(us[i]), 3), "GBps": round(gbs, 1),
                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": qbytes[nme]}
+        if "dynamic" in nme:
+            quant[nme]["note"] = "us per call = amax pass + quantize pass (two launches); bytes = one read + codes"
 
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -14,7 +14,7 @@ import torch
 from ._lib import lib
 
 __all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual", "fp8_quantize_dual_bias_grad",
-           "fp8_amax_fold", "fp8_mm", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
+           "fp8_quantize_dynamic", "DYNAMIC_WORKSPACE_BYTES", "fp8_amax_fold", "fp8_mm", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
 
 E4M3, E5M2 = 0, 1
 F32, F16, BF16 = 0, 1, 2
@@ -23,6 +23,8 @@ _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
 RING_SCRATCH_WORDS = 1024  # FP8MI_RING_SCRATCH_WORDS
+DYNAMIC_WORKSPACE_BYTES = 4096  # FP8MI_DYNAMIC_WORKSPACE_BYTES
+LAYOUT_ROW, LAYOUT_T, LAYOUT_DUAL = 0, 1, 2
 
 
 def ring_words_for(hist_len: int) -> int:
@@ -174,6 +176,35 @@ def fp8_quantize_dual_bias_grad(dy: torch.Tensor, fmt, out_row: torch.Tensor | N
                                              _ptr(amax_out), _ptr(bias_grad_out), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(dy)))
     return out_row, out_t, bias_grad_out
+
+
+def fp8_quantize_dynamic(x: torch.Tensor, fmt, layout: int = LAYOUT_ROW, out_row: torch.Tensor | None = None,
+                         out_t: torch.Tensor | None = None, scale_inv_out: torch.Tensor | None = None,
+                         amax_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Current scaling: quantize a 2-D bf16/fp16/fp32 tensor with
+    s = fmt_max / amax(x) measured in the same call (no ring).  layout 0 row,
+    1 transposed, 2 both; returns (codes or None, codes_t or None)."""
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit column stride")
+    if layout not in (LAYOUT_ROW, LAYOUT_T, LAYOUT_DUAL):
+        raise ValueError(f"layout must be 0, 1 or 2, got {layout!r}")
+    rows, cols = x.shape
+    f = _fmt(fmt)
+    if layout != LAYOUT_T and out_row is None:
+        out_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if layout != LAYOUT_ROW and out_t is None:
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(DYNAMIC_WORKSPACE_BYTES, dtype=torch.uint8, device=x.device)
+    out_row = None if out_row is None else _as_codes(out_row)
+    out_t = None if out_t is None else _as_codes(out_t)
+    ld_x = x.stride(0) if rows > 1 else cols
+    ld_r = 0 if out_row is None else (out_row.stride(0) if out_row.shape[0] > 1 else out_row.shape[1])
+    ld_t = 0 if out_t is None else (out_t.stride(0) if out_t.shape[0] > 1 else out_t.shape[1])
+    _check(lib().fp8_quantize_dynamic(_ptr(x), _DT[x.dtype], rows, cols, ld_x, f, layout, _ptr(out_row), ld_r,
+                                      _ptr(out_t), ld_t, _ptr(scale_inv_out), _ptr(amax_out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(x)))
+    return out_row, out_t
 
 
 def fp8_amax_fold(ring: torch.Tensor, amax: torch.Tensor, fmt) -> None:

@@ -14,6 +14,8 @@ SIGNATURES = {
     "fp8_quantize_dual": (C.c_int, [_P, _I, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _P, _P, _I32, _P, _P, _P]),
     "fp8_quantize_dual_bias_grad": (C.c_int, [_P, _I, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _P, _P, _I32, _P,
                                               _P, _P, _P, C.c_size_t, _P]),
+    "fp8_quantize_dynamic": (C.c_int, [_P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _I64, _P, _P, _P,
+                                       C.c_size_t, _P]),
     "fp8_amax_fold": (C.c_int, [_P, _I32, _P, _I, _P]),
     "fp8_mm": (C.c_int, [_P, _I, _I64, _I64, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P,
                          _I64, _I64, _P]),

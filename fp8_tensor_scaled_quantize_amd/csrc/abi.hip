@@ -42,6 +42,8 @@ int device_cu_count() {
   return cache[dev];
 }
 
+static_assert(kDynWorkspaceBytes == FP8MI_DYNAMIC_WORKSPACE_BYTES, "dynamic workspace size");
+
 static bool valid_fmt(int f) { return f == FP8MI_E4M3 || f == FP8MI_E5M2; }
 static bool valid_dtype(int d) { return d == FP8MI_F32 || d == FP8MI_F16 || d == FP8MI_BF16; }
 static int dtype_bytes(int d) { return d == FP8MI_F32 ? 4 : 2; }
@@ -67,15 +69,9 @@ static fp8mi_status check_input(const void* x, int dt, int64_t rows, int64_t col
   return FP8MI_OK;
 }
 
-static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
-                                    int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
-                                    const float* scale, uint32_t* ring, int32_t H, float* scale_inv_out,
-                                    float* amax_out, void* stream, double* bias_ws = nullptr) {
-  fp8mi_status s = check_input(x, dt, rows, cols, ld_x);
-  if (s != FP8MI_OK) return s;
-  if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
-  s = check_scale_ring(scale, ring, H);
-  if (s != FP8MI_OK) return s;
+static fp8mi_status check_outputs(int mode, int64_t rows, int64_t cols, const uint8_t* out_row, int64_t ld_row,
+                                  const uint8_t* out_t, int64_t ld_t, const float* scale_inv_out,
+                                  const float* amax_out) {
   const bool any = rows > 0 && cols > 0;
   if (mode != 1) {
     if (any && !out_row) return fail(FP8MI_ERR_NULL, "row-layout output is NULL");
@@ -87,9 +83,23 @@ static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t
     if (cols > 0 && ld_t < rows) return fail(FP8MI_ERR_SHAPE, "transposed ld %lld < rows %lld", (long long)ld_t,
                                              (long long)rows);
   }
-  if (reinterpret_cast<uintptr_t>(scale) & 3u || reinterpret_cast<uintptr_t>(scale_inv_out) & 3u ||
-      reinterpret_cast<uintptr_t>(amax_out) & 3u)
+  if (reinterpret_cast<uintptr_t>(scale_inv_out) & 3u || reinterpret_cast<uintptr_t>(amax_out) & 3u)
     return fail(FP8MI_ERR_ARG, "fp32 scalars must be 4-byte aligned");
+  return FP8MI_OK;
+}
+
+static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                                    int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
+                                    const float* scale, uint32_t* ring, int32_t H, float* scale_inv_out,
+                                    float* amax_out, void* stream, double* bias_ws = nullptr) {
+  fp8mi_status s = check_input(x, dt, rows, cols, ld_x);
+  if (s != FP8MI_OK) return s;
+  if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
+  s = check_scale_ring(scale, ring, H);
+  if (s != FP8MI_OK) return s;
+  s = check_outputs(mode, rows, cols, out_row, ld_row, out_t, ld_t, scale_inv_out, amax_out);
+  if (s != FP8MI_OK) return s;
+  if (reinterpret_cast<uintptr_t>(scale) & 3u) return fail(FP8MI_ERR_ARG, "fp32 scalars must be 4-byte aligned");
   hipError_t e = launch_quantize(x, dt, rows, cols, ld_x, fmt, mode, out_row, ld_row, out_t, ld_t, scale, ring, H,
                                  scale_inv_out, amax_out, static_cast<hipStream_t>(stream), bias_ws);
   return from_hip(e, "quantize launch");
@@ -127,6 +137,26 @@ fp8mi_status fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols
                            scale_inv_out, amax_out, stream);
   return quantize_common(x, x_dtype, rows, cols, ld_x, fmt, 0, out, ld_out, nullptr, 0, scale, ring, hist_len,
                          scale_inv_out, amax_out, stream);
+}
+
+fp8mi_status fp8_quantize_dynamic(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                                  int layout, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
+                                  float* scale_inv_out, float* amax_out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (layout < 0 || layout > 2) return fail(FP8MI_ERR_ENUM, "layout must be 0, 1 or 2, got %d", layout);
+  fp8mi_status s = check_input(x, x_dtype, rows, cols, ld_x);
+  if (s != FP8MI_OK) return s;
+  if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
+  s = check_outputs(layout, rows, cols, out_row, ld_row, out_t, ld_t, scale_inv_out, amax_out);
+  if (s != FP8MI_OK) return s;
+  const size_t need = (size_t)kDynWorkspaceBytes;
+  if (!workspace) return fail(FP8MI_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need) return fail(FP8MI_ERR_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(FP8MI_ERR_ARG, "workspace must be 4-byte aligned");
+  return from_hip(launch_quantize_dynamic(x, x_dtype, rows, cols, ld_x, fmt, layout, out_row, ld_row, out_t, ld_t,
+                                          scale_inv_out, amax_out, static_cast<uint32_t*>(workspace),
+                                          static_cast<hipStream_t>(stream)),
+                  "dynamic quantize launch");
 }
 
 fp8mi_status fp8_quantize_dual(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int fmt,

@@ -135,6 +135,20 @@ template <int NT> __device__ __forceinline__ float block_max(float v, float* red
 }
 
 // ---------------------------------------------------------------------------
+// The published scale for a window maximum m: fmt_max / m (IEEE division),
+// or 1.0 when m is 0 or not finite, or the quotient is not a finite positive
+// number.
+// ---------------------------------------------------------------------------
+template <int FMT> __device__ __forceinline__ float scale_from_max(float m) {
+  float s = 1.0f;
+  if (m > 0.0f && m <= 3.40282347e38f) {
+    const float q = FmtTraits<FMT>::kMax / m;
+    if (q > 0.0f && q <= 3.40282347e38f) s = q;
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
 // Ring fold, executed by one full wave (64 lanes): write amax into
 // hist[slot], advance the slot modulo H, publish fmt_max / max(hist) (1.0
 // when that maximum is 0 or not finite, or the quotient is not a finite
@@ -153,11 +167,7 @@ __device__ void ring_fold_wave(uint32_t* ring, int H, float amax, float* scale_i
     if ((uint32_t)i != slot) m = fmaxf(m, hist[i]);
   m = wave_max(m);
   if (lane == 0) {
-    float s = 1.0f;
-    if (m > 0.0f && m <= 3.40282347e38f) {
-      const float q = FmtTraits<FMT>::kMax / m;  // IEEE division
-      if (q > 0.0f && q <= 3.40282347e38f) s = q;
-    }
+    const float s = scale_from_max<FMT>(m);
     reinterpret_cast<float*>(ring)[slot] = amax;
     ring[H] = __float_as_uint(s);
     ring[H + 1] = (slot + 1u == (uint32_t)H) ? 0u : slot + 1u;

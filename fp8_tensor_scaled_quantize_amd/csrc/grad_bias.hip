@@ -160,13 +160,7 @@ template <int FMT> __global__ void ring_seed_kernel(uint32_t* ring, int H, const
   for (int i = t; i < H + 4 + kFoldSlots * kFoldSlotStride; i += blockDim.x)
     if (i != H) ring[i] = 0u;
   if (t == 0) {
-    const float m = *amax;
-    float s = 1.0f;
-    if (m > 0.0f && m <= 3.40282347e38f) {
-      const float q = FmtTraits<FMT>::kMax / m;
-      if (q > 0.0f && q <= 3.40282347e38f) s = q;
-    }
-    ring[H] = __float_as_uint(s);
+    ring[H] = __float_as_uint(scale_from_max<FMT>(*amax));
   }
 }
 

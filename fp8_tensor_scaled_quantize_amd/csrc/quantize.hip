@@ -43,11 +43,47 @@ struct QuantArgs {
   float* scale_inv_out;
   float* amax_out;
   double* bias_ws;      // dual with bias gradient: fp64 column sums per 128-row tile, [tile row][col]
+  const uint32_t* parts;  // current scaling: per-workgroup amax partials (fp32 bits), or null
+  int nparts;
 };
 
+// Max over the current-scaling partials (n >= 1), computed by one whole wave;
+// the result is valid in every lane.  The partials are non-negative fp32 bit
+// patterns, which order like their values, so an integer max is exact and
+// independent of order.
+__device__ __forceinline__ float parts_max(const uint32_t* parts, int n) {
+  constexpr int kLoads = 16;  // 1024 partials (a full workspace) in one batch
+  const int lane = threadIdx.x & 63;
+  uint32_t m = 0;
+  for (int base = 0; base < n; base += 64 * kLoads) {
+    uint32_t v[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int i = base + 64 * j + lane;
+      v[j] = parts[i < n ? i : n - 1];  // a repeated partial leaves the max unchanged
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) m = max(m, v[j]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  return __uint_as_float(m);
+}
+
 // Shared ending of every quantize workgroup.
-template <int FMT, int NT>
+template <int FMT, int NT, bool DYN>
 __device__ __forceinline__ void quant_block_done(const QuantArgs& p, float thread_amax, float s, float* red) {
+  if constexpr (DYN) {
+    // current scaling: amax was measured by the partials pass; no atomics
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
+      const float a = parts_max(p.parts, p.nparts);
+      if (threadIdx.x == 0) {
+        if (p.amax_out) *p.amax_out = a;
+        if (p.scale_inv_out) *p.scale_inv_out = 1.0f / s;
+      }
+    }
+    return;
+  }
   const float bmax = block_max<NT>(thread_amax, red);
   if (p.ring) {
     ring_block_done<FMT>(p.ring, p.H, bmax, s, p.scale_inv_out, p.amax_out, reinterpret_cast<uint32_t*>(red));
@@ -108,8 +144,13 @@ template <int N> __device__ __forceinline__ float nan_free_absmax(const float* f
   return m;
 }
 
-template <int FMT> __device__ __forceinline__ float read_scale(const QuantArgs& p) {
-  return p.ring ? __uint_as_float(p.ring[p.H]) : *p.scale;
+// The scale this call quantizes with: measured from the partials (DYN,
+// current scaling), else the ring's current scale (delayed scaling) or the
+// caller's.  DYN is a template parameter so that the delayed-scaling kernels
+// carry none of the partials code (it would cost them registers).
+template <int FMT, bool DYN> __device__ __forceinline__ float read_scale(const QuantArgs& p) {
+  if constexpr (DYN) return scale_from_max<FMT>(parts_max(p.parts, p.nparts));
+  else return p.ring ? __uint_as_float(p.ring[p.H]) : *p.scale;
 }
 
 // ===========================================================================
@@ -168,7 +209,7 @@ __device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t
 // persistent grids over large tensors; without it a block holds one group
 // at a time, which keeps registers low and occupancy high for the grids that
 // give every workgroup a single group.
-template <int DT, int FMT, bool PF>
+template <int DT, int FMT, bool PF, bool DYN>
 __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64_t n, int64_t steps_per_block) {
   __shared__ float red[kFlatThreads / 64];
   constexpr int EB = In<DT>::kBytes;
@@ -196,7 +237,7 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
   uint4 va[U][NL];
   if (ng > 0) load_group(va, first);
   // the scale is read after the first loads are out (it does not gate them)
-  const float s = read_scale<FMT>(p);
+  const float s = read_scale<FMT, DYN>(p);
   auto encode_group = [&](const uint4 (&v)[U][NL], int64_t g0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -245,7 +286,7 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
       }
     }
   }
-  quant_block_done<FMT, kFlatThreads>(p, amax, s, red);
+  quant_block_done<FMT, kFlatThreads, DYN>(p, amax, s, red);
 }
 
 // ===========================================================================
@@ -263,14 +304,14 @@ __device__ __forceinline__ int lds_t_index(int c, int w) { return c * 32 + (w ^ 
 
 // One-shot form: each workgroup loads, encodes and stores its tiles in turn
 // (launched with one tile per workgroup; low registers, high occupancy).
-template <int DT, int FMT, int MODE, bool BG = false>
+template <int DT, int FMT, int MODE, bool BG, bool DYN>
 __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int64_t tiles_c, int64_t ntiles,
                                                                 int64_t tiles_per_block) {
   __shared__ float red[kTileThreads / 64];
   __shared__ __align__(16) uint32_t lds_t[(MODE == kRow) ? 1 : kTileC * 32];
   __shared__ double bg_red[BG ? kTileThreads / 64 : 1][BG ? kTileC : 1];
   constexpr int EB = In<DT>::kBytes;
-  const float s = read_scale<FMT>(p);
+  const float s = read_scale<FMT, DYN>(p);
   const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
   float amax = 0.0f;
   const char* xb = static_cast<const char*>(p.x);
@@ -416,7 +457,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
       __syncthreads();  // LDS reused by the next tile
     }
   }
-  quant_block_done<FMT, kTileThreads>(p, amax, s, red);
+  quant_block_done<FMT, kTileThreads, DYN>(p, amax, s, red);
 }
 
 // Persistent form (quantize_tiled_pf).  One tile's raw input for this thread: rows 4rg..4rg+3 at columns
@@ -429,7 +470,7 @@ template <int DT> struct TileRaw {
   uint32_t full;  // bit i: row i came through vector loads
 };
 
-template <int DT, int FMT, int MODE, bool BG = false>
+template <int DT, int FMT, int MODE, bool BG, bool DYN>
 __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, int64_t tiles_c, int64_t ntiles,
                                                                 int64_t tiles_per_block) {
   __shared__ float red[kTileThreads / 64];
@@ -602,13 +643,13 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
   // waits only for that prefetch).
   TileRaw<DT> cur, nxt;
   if (t_first < t_last) load_tile(t_first, cur);
-  const float s = read_scale<FMT>(p);  // after the first loads are out
+  const float s = read_scale<FMT, DYN>(p);  // after the first loads are out
   for (int64_t tile = t_first; tile < t_last; ++tile) {
     if (tile + 1 < t_last) load_tile(tile + 1, nxt);
     process_tile(tile, cur, s);
     cur = nxt;
   }
-  quant_block_done<FMT, kTileThreads>(p, amax, s, red);
+  quant_block_done<FMT, kTileThreads, DYN>(p, amax, s, red);
 }
 
 // Fold alone / arming of a ring-less amax output.
@@ -617,6 +658,118 @@ template <int FMT> __global__ void amax_fold_kernel(uint32_t* ring, int H, const
 }
 __global__ void zero_word_kernel(float* p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0.0f;
+}
+
+// ===========================================================================
+// Current scaling, first pass.  Every workgroup writes the NaN-free max |x| of
+// its share of the input to parts[blockIdx.x] as fp32 bits; the quantize pass
+// that follows reads all partials in every wave (see read_scale), so there
+// are no atomics and no workgroup ever waits on another.
+// Contiguous input (ld_x == cols, or one row): the body of 16-byte chunks is
+// shared grid-stride, kAmaxLoads chunks in flight per lane; the unaligned head
+// and the ragged tail (fewer than 16 bytes each) go element by element in
+// workgroup 0.  Strided rows: one wave per row at a time, same split per row.
+// ===========================================================================
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxLoads = 8;
+constexpr int kAmaxBlocksPerCU = 4;
+constexpr int kDynSlots = 1024;  // partials capacity of the caller's workspace
+
+// |x| of one element as a key that orders like the magnitude: the magnitude
+// bits of the element's own format, NaN mapped to 0.
+template <int DT> struct AmaxKey {
+  static constexpr uint32_t kMag = DT == kF32 ? 0x7FFFFFFFu : 0x7FFFu;
+  static constexpr uint32_t kInf = DT == kF32 ? 0x7F800000u : (DT == kF16 ? 0x7C00u : 0x7F80u);
+  __device__ static __forceinline__ uint32_t key(uint32_t raw) {
+    const uint32_t m = raw & kMag;
+    return m > kInf ? 0u : m;
+  }
+  __device__ static __forceinline__ uint32_t chunk(const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (DT == kF32) {
+        m = max(m, key(w[e]));
+      } else {
+        m = max(m, key(w[e]));  // low half (key masks the high half away)
+        m = max(m, key(w[e] >> 16));
+      }
+    }
+    return m;
+  }
+  __device__ static __forceinline__ uint32_t raw(const char* xb, int64_t i) {
+    if constexpr (DT == kF32) return reinterpret_cast<const uint32_t*>(xb)[i];
+    else return reinterpret_cast<const uint16_t*>(xb)[i];
+  }
+  // fp32 bits of the magnitude a key stands for (exact widening)
+  __device__ static __forceinline__ uint32_t f32_bits(uint32_t k) {
+    if constexpr (DT == kF32) return k;
+    else if constexpr (DT == kBF16) return k << 16;
+    else return __float_as_uint(f16_to_f32(k));
+  }
+};
+
+// Key max of n contiguous elements at xb, spread over `nthr` threads of which
+// this is number `tid`; 16-byte chunks in the middle, elements at the ends.
+template <int DT>
+__device__ __forceinline__ uint32_t segment_amax_key(const char* xb, int64_t n, int64_t tid, int64_t nthr) {
+  using K = AmaxKey<DT>;
+  constexpr int EB = In<DT>::kBytes, EPC = 16 / EB;
+  const int64_t lead = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(xb) & 15u)) & 15u) / EB);
+  const int64_t head = lead < n ? lead : n;
+  const int64_t nch = (n - head) / EPC;
+  const int64_t tail0 = head + nch * EPC;
+  const uint4* body = reinterpret_cast<const uint4*>(xb + head * EB);
+  uint32_t m = 0;
+  // batches of kAmaxLoads chunks per thread, all loads issued before any is
+  // used; past the end a thread re-reads the last chunk (harmless for a max),
+  // so the loads stay unconditional
+  for (int64_t c = tid; c < nch; c += kAmaxLoads * nthr) {
+    uint4 v[kAmaxLoads];
+#pragma unroll
+    for (int j = 0; j < kAmaxLoads; ++j) {
+      const int64_t i = c + j * nthr;
+      v[j] = body[i < nch ? i : nch - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kAmaxLoads; ++j) m = max(m, K::chunk(v[j]));
+  }
+  if (tid < EPC) {
+    if (tid < head) m = max(m, K::key(K::raw(xb, tid)));
+    if (tail0 + tid < n) m = max(m, K::key(K::raw(xb, tail0 + tid)));
+  }
+  return m;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kAmaxThreads) amax_partials(const void* x, int64_t rows, int64_t cols,
+                                                             int64_t ld_x, uint32_t* parts) {
+  using K = AmaxKey<DT>;
+  constexpr int EB = In<DT>::kBytes;
+  __shared__ uint32_t red[kAmaxThreads / 64];
+  const char* xb = static_cast<const char*>(x);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t m = 0;
+  if (ld_x == cols || rows == 1) {
+    const int64_t nthr = (int64_t)gridDim.x * kAmaxThreads;
+    const int64_t tid = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    m = segment_amax_key<DT>(xb, rows * cols, tid, nthr);
+  } else {
+    const int64_t nw = (int64_t)gridDim.x * (kAmaxThreads / 64);
+    for (int64_t r = (int64_t)blockIdx.x * (kAmaxThreads / 64) + wid; r < rows; r += nw)
+      m = max(m, segment_amax_key<DT>(xb + r * ld_x * EB, cols, lane, 64));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if (lane == 0) red[wid] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = red[0];
+#pragma unroll
+    for (int w = 1; w < kAmaxThreads / 64; ++w) b = max(b, red[w]);
+    parts[blockIdx.x] = K::f32_bits(b);
+  }
 }
 
 // ===========================================================================
@@ -638,18 +791,18 @@ static int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-template <int DT, int FMT, int M, bool BG = false>
+template <int DT, int FMT, int M, bool BG, bool DYN>
 static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantArgs& p, int64_t tiles_c,
                          int64_t ntiles, int64_t tpb) {
   if (one_shot) {
-    hipLaunchKernelGGL((quantize_tiled<DT, FMT, M, BG>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
+    hipLaunchKernelGGL((quantize_tiled<DT, FMT, M, BG, DYN>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
   } else {
-    hipLaunchKernelGGL((quantize_tiled_pf<DT, FMT, M, BG>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles,
+    hipLaunchKernelGGL((quantize_tiled_pf<DT, FMT, M, BG, DYN>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles,
                        tpb);
   }
 }
 
-template <int DT, int FMT>
+template <int DT, int FMT, bool DYN>
 static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int ncu = device_cu_count();
   static const int persist_bpc = env_int("FP8MI_Q_BPC", kPersistBlocksPerCU);
@@ -661,11 +814,11 @@ static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
     const int64_t steps = cdiv(n, kFlatBlockStep);
     if (steps <= (int64_t)ncu * kOneShotBlocksPerCU * kFlatUnroll) {
       const int64_t spb = kFlatUnroll, blocks = steps == 0 ? 1 : cdiv(steps, spb);
-      hipLaunchKernelGGL((quantize_flat<DT, FMT, false>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n,
+      hipLaunchKernelGGL((quantize_flat<DT, FMT, false, DYN>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n,
                          spb);
     } else {
       const int64_t spb = cdiv(steps, (int64_t)ncu * persist_bpc), blocks = cdiv(steps, spb);
-      hipLaunchKernelGGL((quantize_flat<DT, FMT, true>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n,
+      hipLaunchKernelGGL((quantize_flat<DT, FMT, true, DYN>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n,
                          spb);
     }
     return hipGetLastError();
@@ -676,26 +829,26 @@ static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int64_t tpb = one_shot ? 1 : cdiv(ntiles, (int64_t)ncu * persist_bpc);
   const dim3 grid((unsigned)cdiv(ntiles, tpb));
   switch (mode) {
-    case kRow: launch_tiled<DT, FMT, kRow>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
-    case kTrans: launch_tiled<DT, FMT, kTrans>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
+    case kRow: launch_tiled<DT, FMT, kRow, false, DYN>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
+    case kTrans: launch_tiled<DT, FMT, kTrans, false, DYN>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
     default:
-      if constexpr (DT != kF32) {
+      if constexpr (DT != kF32 && !DYN) {
         if (p.bias_ws) {
-          launch_tiled<DT, FMT, kDual, true>(one_shot, grid, st, p, tiles_c, ntiles, tpb);
+          launch_tiled<DT, FMT, kDual, true, false>(one_shot, grid, st, p, tiles_c, ntiles, tpb);
           break;
         }
       }
-      launch_tiled<DT, FMT, kDual>(one_shot, grid, st, p, tiles_c, ntiles, tpb);
+      launch_tiled<DT, FMT, kDual, false, DYN>(one_shot, grid, st, p, tiles_c, ntiles, tpb);
       break;
   }
   return hipGetLastError();
 }
 
-template <int FMT> static hipError_t launch_fmt(const QuantArgs& p, int dt, int mode, hipStream_t st) {
+template <int FMT, bool DYN> static hipError_t launch_fmt(const QuantArgs& p, int dt, int mode, hipStream_t st) {
   switch (dt) {
-    case kF32: return launch_dt_fmt<kF32, FMT>(p, mode, st);
-    case kF16: return launch_dt_fmt<kF16, FMT>(p, mode, st);
-    default: return launch_dt_fmt<kBF16, FMT>(p, mode, st);
+    case kF32: return launch_dt_fmt<kF32, FMT, DYN>(p, mode, st);
+    case kF16: return launch_dt_fmt<kF16, FMT, DYN>(p, mode, st);
+    default: return launch_dt_fmt<kBF16, FMT, DYN>(p, mode, st);
   }
 }
 
@@ -703,13 +856,52 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
                            uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t, const float* scale,
                            uint32_t* ring, int H, float* scale_inv_out, float* amax_out, hipStream_t st,
                            double* bias_ws) {
-  QuantArgs p{x, rows, cols, ld_x, out_row, ld_row, out_t, ld_t, scale, ring, H, scale_inv_out, amax_out, bias_ws};
+  QuantArgs p{x, rows, cols, ld_x, out_row, ld_row, out_t, ld_t, scale, ring, H, scale_inv_out, amax_out, bias_ws,
+              nullptr, 0};
   if (!ring && amax_out) {
     hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, st, amax_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return fmt == kE4M3 ? launch_fmt<kE4M3>(p, dt, mode, st) : launch_fmt<kE5M2>(p, dt, mode, st);
+  return fmt == kE4M3 ? launch_fmt<kE4M3, false>(p, dt, mode, st) : launch_fmt<kE5M2, false>(p, dt, mode, st);
+}
+
+int64_t dynamic_workspace_bytes() { return (int64_t)kDynSlots * 4; }
+
+// Current scaling: the partials pass, then the ordinary quantize kernels with
+// the scale measured from the partials.
+hipError_t launch_quantize_dynamic(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                                   int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
+                                   float* scale_inv_out, float* amax_out, uint32_t* parts, hipStream_t st) {
+  const int ncu = device_cu_count();
+  static const int amax_bpc = env_int("FP8MI_AMAX_BPC", kAmaxBlocksPerCU);
+  const int eb = dt == kF32 ? 4 : 2;
+  // as few load batches per thread as the cap allows, spread evenly (a
+  // half-filled last batch would cost a whole extra round trip)
+  const int64_t chunks = rows * cols * eb / 16 + 1;
+  const int64_t per_block = (int64_t)kAmaxThreads * kAmaxLoads;
+  const int64_t cap = (int64_t)ncu * amax_bpc < kDynSlots ? (int64_t)ncu * amax_bpc : kDynSlots;
+  const int64_t batches = cdiv(chunks, cap * per_block);
+  int64_t nb = cdiv(chunks, per_block * batches);
+  if (nb > cap) nb = cap;
+  if (!(ld_x == cols || rows == 1)) {
+    const int64_t rb = cdiv(rows, kAmaxThreads / 64);  // a wave per row: no more blocks than rows / 4
+    if (nb > rb) nb = rb;
+  }
+  if (nb < 1) nb = 1;
+  switch (dt) {
+    case kF32: hipLaunchKernelGGL(amax_partials<kF32>, dim3((unsigned)nb), dim3(kAmaxThreads), 0, st, x, rows, cols,
+                                  ld_x, parts); break;
+    case kF16: hipLaunchKernelGGL(amax_partials<kF16>, dim3((unsigned)nb), dim3(kAmaxThreads), 0, st, x, rows, cols,
+                                  ld_x, parts); break;
+    default: hipLaunchKernelGGL(amax_partials<kBF16>, dim3((unsigned)nb), dim3(kAmaxThreads), 0, st, x, rows, cols,
+                                ld_x, parts); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  QuantArgs p{x, rows, cols, ld_x, out_row, ld_row, out_t, ld_t, nullptr, nullptr, 0, scale_inv_out, amax_out,
+              nullptr, parts, (int)nb};
+  return fmt == kE4M3 ? launch_fmt<kE4M3, true>(p, dt, mode, st) : launch_fmt<kE5M2, true>(p, dt, mode, st);
 }
 
 hipError_t launch_amax_fold(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st) {

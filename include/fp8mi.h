@@ -122,6 +122,35 @@ FP8MI_API fp8mi_status fp8_quantize_dual(const void* x, int x_dtype, int64_t row
                                float* scale_inv_out, float* amax_out, void* stream);
 
 /*
+ * fp8_quantize_dynamic -- current (dynamic) scaling: the scale is measured
+ * from x itself and used by the same call, with no ring (log:tests/extension,
+ * the commit merging the delayed and dynamic recipes behind one `dynamic`
+ * flag and the commit that allocates no scale rings on the dynamic path,
+ * whose scales are measured inline).  s = fmt_max / amax(x) -- or 1.0 when
+ * amax is 0 or not finite or the quotient is not a finite positive number,
+ * exactly the scale a ring fold of amax(x) into an empty window publishes --
+ * and x is quantized with s as in fp8_quantize.
+ *   layout     0: row layout into out_row (ld_row >= cols); 1: transposed into
+ *              out_t (ld_t >= rows); 2: both, from one read.  The pointer of an
+ *              unused layout is ignored.
+ *   scale_inv_out  optional device fp32: 1 / s, the dequantisation multiplier.
+ *   amax_out   optional device fp32: amax(x).
+ *   workspace  device scratch of at least FP8MI_DYNAMIC_WORKSPACE_BYTES bytes,
+ *              4-byte aligned, owned by the caller, no initialisation (it
+ *              carries per-workgroup partial maxima from the first launch to
+ *              the second); calls in flight on one workspace race.
+ * Other arguments as fp8_quantize.  Two launches on `stream`: an amax pass
+ * over x, then the quantize pass, whose workgroups each reduce the partials to
+ * s.  rows * cols == 0 gives amax 0 and s = 1.  A missing or short workspace
+ * returns FP8MI_ERR_NULL / FP8MI_ERR_ARG before any launch.
+ */
+#define FP8MI_DYNAMIC_WORKSPACE_BYTES 4096
+FP8MI_API fp8mi_status fp8_quantize_dynamic(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                            int fmt, int layout, uint8_t* out_row, int64_t ld_row, uint8_t* out_t,
+                                            int64_t ld_t, float* scale_inv_out, float* amax_out, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
  * fp8_amax_fold -- the ring fold alone, for an amax already on the device
  * (e.g. one reduced over several devices): one tiny launch that performs
  * exactly the fold a ring-mode quantize performs in its last workgroup

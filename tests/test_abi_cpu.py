@@ -169,3 +169,34 @@ def test_ring_seed_rejects(L):
     assert f(FAKE, 4, FAKE, 3, None) == ENUM
     assert f(FAKE, 0, FAKE, 0, None) == SHAPE
     assert f(FAKE + 2, 4, FAKE, 0, None) == ARG
+
+
+def test_quantize_dynamic_rejects(L):
+    f = L.fp8_quantize_dynamic
+    W = 4096  # FP8MI_DYNAMIC_WORKSPACE_BYTES
+    header = open(os.path.join(ROOT, "include", "fp8mi.h")).read()
+    assert re.search(r"#define FP8MI_DYNAMIC_WORKSPACE_BYTES\s+4096\b", header)
+
+    def call(x=FAKE, dt=2, rows=4, cols=4, ld=4, fmt=0, layout=0, o_row=FAKE, ld_r=4, o_t=FAKE, ld_t=4,
+             sinv=None, amax=None, ws=FAKE, wsb=W):
+        return f(x, dt, rows, cols, ld, fmt, layout, o_row, ld_r, o_t, ld_t, sinv, amax, ws, wsb, None)
+
+    assert call(layout=3) == ENUM
+    assert call(layout=-1) == ENUM
+    assert call(dt=7) == ENUM
+    assert call(fmt=2) == ENUM
+    assert call(rows=-1) == SHAPE
+    assert call(ld=3) == SHAPE
+    assert call(x=None) == NULL
+    assert call(x=FAKE + 1) == ARG          # bf16 input not 2-byte aligned
+    assert call(o_row=None) == NULL          # row layout needs out_row
+    assert call(layout=1, o_t=None) == NULL  # transposed layout needs out_t
+    assert call(layout=2, o_row=None) == NULL
+    assert call(layout=1, ld_t=3) == SHAPE
+    assert call(ld_r=3) == SHAPE
+    assert call(sinv=FAKE + 2) == ARG
+    assert call(amax=FAKE + 1) == ARG
+    assert call(ws=None) == NULL             # workspace missing, even for an empty tensor
+    assert call(ws=None, rows=0) == NULL
+    assert call(wsb=W - 4) == ARG            # workspace too small
+    assert call(ws=FAKE + 2) == ARG          # workspace not 4-byte aligned

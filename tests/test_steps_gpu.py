@@ -164,3 +164,78 @@ def test_full_training_step_32_steps():
         db_gpu = np_bf16_bits(db)
         assert O.within_tolerance(db_gpu, db_ref, db_mag).all(), t
         assert (db_gpu == db_ref).mean() > 0.999, t
+
+
+def test_tiny_dynamic_scaling_steps():
+    """The layer under the dynamic recipe: every step's scales come from that
+    step's own tensors (an amax jump is followed at once), codes and scale
+    snapshots bit-exact, Y / dX / dW within the GEMM bound, db exact."""
+    xs, w, b = tiny_inputs(4)
+    xs[2] = synth.f32_to_bf16_bits(O.widen_to_f32(xs[2], "bf16") * np.float32(10.0))
+    dys = [synth.gaussian((64, 256), 1e-3, "bf16", 1, synth.T_DY, t) for t in range(4)]
+    layer = Fp8Linear(dev_bf16(w), dev_bf16(b), dynamic=True)
+    assert layer.ring_x is None
+    layer.seed(dev_bf16(xs[0]))  # no-op under dynamic scaling
+    bias = O.widen_to_f32(b, "bf16").astype(np.float64)
+    qw = O.quantize_dynamic(w, "bf16", O.E4M3)
+    for t in range(4):
+        qx = O.quantize_dynamic(xs[t], "bf16", O.E4M3)
+        qg = O.quantize_dynamic(dys[t], "bf16", O.E5M2)
+        y = layer.forward(dev_bf16(xs[t]))
+        dx, dw, db = layer.backward(dev_bf16(dys[t]))
+        torch.cuda.synchronize()
+        xq, wq = layer.last_codes
+        gq, gq_t = layer.last_grad_codes
+        assert np.array_equal(np_codes(xq), qx["codes"]), t
+        assert np.array_equal(np_codes(wq), qw["codes"]), t
+        assert np.array_equal(np_codes(gq), qg["codes"]) and np.array_equal(np_codes(gq_t), qg["codes_t"]), t
+        si = f32_words(layer.scale_inv)
+        assert list(si) == [as_bits(qx["scale_inv"]), as_bits(qw["scale_inv"]), as_bits(qg["scale_inv"])], t
+        check(np_bf16_bits(y), qx["codes"], O.E4M3, qw["codes"], O.E4M3, qx["scale_inv"], qw["scale_inv"], bias,
+              tag=f"dyn Y {t}")
+        check(np_bf16_bits(dx), qg["codes"], O.E5M2, qw["codes_t"], O.E4M3, qg["scale_inv"], qw["scale_inv"], None,
+              tag=f"dyn dX {t}")
+        check(np_bf16_bits(dw), qg["codes_t"], O.E5M2, qx["codes_t"], O.E4M3, qg["scale_inv"], qx["scale_inv"],
+              None, tag=f"dyn dW {t}")
+        assert np.array_equal(np_bf16_bits(db), O.grad_bias(dys[t])[0]), t
+    # the step with the 10x amax used a 10x smaller scale at once (no delay)
+    assert O.quantize_dynamic(xs[2], "bf16", O.E4M3)["scale_inv"] > O.quantize_dynamic(xs[1], "bf16",
+                                                                                        O.E4M3)["scale_inv"]
+
+
+def test_full_shape_dynamic_step():
+    """Two dynamic steps at the training shape (x [4,2048,1536], W
+    [6912,1536], dY [8192,6912]): scale snapshots exact, codes and GEMM rows
+    on seeded samples."""
+    M, K, N = 8192, 1536, 6912
+    w = synth.gaussian((N, K), 0.02, "bf16", 7, synth.T_W, 0)
+    b = synth.gaussian((N,), 0.1, "bf16", 7, synth.T_BIAS, 0)
+    wf, bias = O.widen_to_f32(w, "bf16"), O.widen_to_f32(b, "bf16").astype(np.float64)
+    layer = Fp8Linear(dev_bf16(w), dev_bf16(b), dynamic=True)
+    sw = O.next_scale(np.array([O.amax(wf)]), O.E4M3)
+    wc = O.encode(O.scaled_values(wf, sw), O.E4M3)
+    for t in range(2):
+        x = synth.gaussian((M, K), 1.0, "bf16", 7, synth.T_X, t)
+        dy = synth.gaussian((M, N), 1e-3 * (1 + 9 * t), "bf16", 7, synth.T_DY, t)
+        y = layer.forward(dev_bf16(x).view(4, 2048, K))
+        dx, dw, db = layer.backward(dev_bf16(dy))
+        torch.cuda.synchronize()
+        xf, gf = O.widen_to_f32(x, "bf16"), O.widen_to_f32(dy, "bf16")
+        sx = O.next_scale(np.array([O.amax(xf)]), O.E4M3)
+        sg = O.next_scale(np.array([O.amax(gf)]), O.E5M2)
+        si = f32_words(layer.scale_inv)
+        assert list(si) == [as_bits(O.scale_inv(s)) for s in (sx, sw, sg)], t
+        rs = np.sort(synth.rng(8, t, 0).choice(M, 32, replace=False))
+        xq_rows = O.encode(O.scaled_values(xf[rs], sx), O.E4M3)
+        gq_rows = O.encode(O.scaled_values(gf[rs], sg), O.E5M2)
+        xq, wq = layer.last_codes
+        gq, _ = layer.last_grad_codes
+        assert np.array_equal(np_codes(xq[rs]), xq_rows), t
+        assert np.array_equal(np_codes(gq[rs]), gq_rows), t
+        assert np.array_equal(np_codes(wq), wc), t
+        check(np_bf16_bits(y.reshape(M, N))[rs], xq_rows, O.E4M3, wc, O.E4M3, O.scale_inv(sx), O.scale_inv(sw),
+              bias, tag=f"dyn Y {t}")
+        check(np_bf16_bits(dx.reshape(M, K))[rs], gq_rows, O.E5M2, np.ascontiguousarray(wc.T), O.E4M3,
+              O.scale_inv(sg), O.scale_inv(sw), None, tag=f"dyn dX {t}")
+        db_ref, db_mag = O.grad_bias(dy)
+        assert np.array_equal(np_bf16_bits(db), db_ref), t
