@@ -355,6 +355,39 @@ def within_tolerance(gpu_bits, ref_bits, abs_sum, rel=1e-5):
     return ok | ((g == r) & ~np.isnan(g))
 
 
+# --------------------------------------------------------------------------
+# O14/O15: fp8-stored bias and the quantizing (FP8-out) GEMM epilogue.
+# --------------------------------------------------------------------------
+def dequant_bias(codes: np.ndarray, fmt: str, bias_scale) -> np.ndarray:
+    """An fp8-stored bias as the epilogue uses it: fl32(dec(code) * s_b), one
+    fp32 multiply of the code's exact value by the bias scale, applied after
+    the operand scaling and before any output quantization (log:tests/extension,
+    the commit giving the bias a bias_scale slot: no scale = a bf16 bias, a
+    scale = fp8 storage dequantized in the epilogue)."""
+    return scaled_values(decode_table(fmt)[np.asarray(codes, dtype=np.uint8)].astype(np.float32), bias_scale)
+
+
+def mm_quantized(a_codes, fmt_a, b_codes, fmt_b, fmt_c, a_scale_inv=1.0, b_scale_inv=1.0, bias=None,
+                 scale=None, ring: Ring | None = None):
+    """FP8-in / FP8-out GEMM (log:tests/extension, the commit adding the
+    FP8-in/FP8-out GEMM op; the output quantization comes after the bias, per
+    the bias_scale commit).  The pre-quantization output is the GEMM's value
+    y (mm_exact_f64) held in fp32, fl32(y); it is then quantized exactly as a
+    quantize call quantizes an fp32 tensor: codes enc(fl32(fl32(y) * s_c)),
+    amax over fl32(y) (NaN ignored, every batch together), s_c explicit or the
+    ring's current scale, and one fold of that amax into the ring.  Returns
+    the quantize dict (codes shaped like y) plus y and abs_sum for the
+    tolerance."""
+    y, mag = mm_exact_f64(a_codes, fmt_a, b_codes, fmt_b, a_scale_inv, b_scale_inv, bias)
+    with np.errstate(over="ignore"):
+        y32 = y.astype(np.float32)
+    q = quantize(y32.reshape(-1, y32.shape[-1]), F32, fmt_c, scale=scale, ring=ring)
+    out = {k: q[k] for k in ("amax", "scale_inv", "ring")}
+    out["codes"] = q["codes"].reshape(y.shape)
+    out["y"], out["abs"] = y, mag
+    return out
+
+
 def grad_bias(dy_bits: np.ndarray, dtype: str = BF16):
     """Bias gradient: sum of the bf16 (or fp16) upstream gradient over every
     leading dimension, summed in float64 and rounded once to bf16

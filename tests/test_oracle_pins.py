@@ -551,3 +551,76 @@ def test_dynamic_equals_delayed_with_a_ring_seeded_from_the_same_tensor():
         d = O.quantize(x, dtype, O.E5M2, ring=O.seed_ring(4, x, dtype, O.E5M2))
         assert np.array_equal(r["codes"], d["codes"])
         assert r["scale_inv"] == d["scale_inv"] and r["amax"] == d["amax"]
+
+
+# --------------------------------------------- fp8 bias, FP8-out GEMM ----
+@pytest.mark.parametrize("fmt", O.FORMATS)
+def test_dequant_bias_matches_torch_widen_times_scale(fmt):
+    """fl32(dec(code) * s) for every code and several scales, against torch's
+    own fp8 -> fp32 cast followed by an fp32 multiply."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref_dec = torch.from_numpy(codes).view(TORCH_FP8[fmt]).to(torch.float32)
+    for s in (1.0, 0.5, 3.0e-3, 771.25):
+        got = O.dequant_bias(codes, fmt, s)
+        ref = (ref_dec * torch.tensor(np.float32(s))).numpy()
+        assert np.array_equal(got.view(np.uint32)[~np.isnan(ref)], ref.view(np.uint32)[~np.isnan(ref)])
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def _mm_golden_rows():
+    for line in open(os.path.join(GOLDEN, "mm_fp8_out_worked.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            yield line.split()
+
+
+def _mm_golden_case(f):
+    case, fmt_c, bcodes, sa, sb, bias, scale = f[:7]
+    a = np.array([[0x38, 0x40]], np.uint8)
+    b = np.array([[int(c, 16) for c in row.split(",")] for row in bcodes.split(";")], np.uint8)
+    bias_v = None
+    if bias.startswith("f32:"):
+        bias_v = np.array([float(v) for v in bias[4:].split(",")], np.float32).astype(np.float64)
+    elif bias.startswith("e4m3:"):
+        codes, bs = bias[5:].split("@")
+        bias_v = O.dequant_bias(np.array([int(c, 16) for c in codes.split(",")], np.uint8), O.E4M3,
+                                float(bs)).astype(np.float64)
+    kind, val = scale.split(":")
+    kw = {"scale": float(val)} if kind == "explicit" else {"ring": O.Ring.new(2, float(val))}
+    return case, a, b, float(sa), float(sb), bias_v, fmt_c, kw
+
+
+def test_mm_quantized_golden_worked():
+    n = 0
+    for f in _mm_golden_rows():
+        case, a, b, sa, sb, bias_v, fmt_c, kw = _mm_golden_case(f)
+        codes, amax, sinv, ring_after = f[7:11]
+        r = O.mm_quantized(a, O.E4M3, b, O.E4M3, fmt_c, sa, sb, bias_v, **kw)
+        assert r["codes"][0, 0].tolist() == [int(c, 16) for c in codes.split(",")], case
+        assert r["amax"] == np.float32(float(amax)), case
+        assert r["scale_inv"] == np.float32(float(sinv)), case
+        if ring_after != "-":
+            sc, idx, hist = ring_after.split(",")
+            assert r["ring"].scale == np.float32(float(sc)) and r["ring"].idx == int(idx), case
+            assert r["ring"].hist.tolist() == [float(h) for h in hist.split(":")], case
+        else:
+            assert r["ring"] is None
+        n += 1
+    assert n == 6
+
+
+def test_mm_quantized_is_quantize_of_the_exact_gemm():
+    """Small-integer codes make every y exact (the integer-GEMM pin); then the
+    output codes must be a quantize of those exact values, batch and all."""
+    g = synth.rng(93)
+    vals = np.arange(-6, 7)
+    enc = {v: int(O.encode(np.array([v], np.float32), O.E4M3)[0]) for v in vals}
+    a = np.vectorize(enc.get)(g.choice(vals, (2, 9, 32))).astype(np.uint8)
+    b = np.vectorize(enc.get)(g.choice(vals, (2, 7, 32))).astype(np.uint8)
+    ia, ib = O.decode_table(O.E4M3)[a], O.decode_table(O.E4M3)[b]
+    y = np.einsum("bik,bjk->bij", ia, ib) * 0.25 + np.arange(7)[None, None, :]
+    ring = O.Ring.new(3, 2.0)
+    r = O.mm_quantized(a, O.E4M3, b, O.E4M3, O.E5M2, 0.5, 0.5, np.arange(7, dtype=np.float64), ring=ring)
+    q = O.quantize(y.reshape(-1, 7).astype(np.float32), O.F32, O.E5M2, ring=ring)
+    assert np.array_equal(r["codes"].reshape(-1, 7), q["codes"])
+    assert r["amax"] == np.float32(np.abs(y).max()) and r["ring"].words().tolist() == q["ring"].words().tolist()
