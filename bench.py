@@ -222,7 +222,9 @@ def main():
     total_ms = timed(lambda i: step(args.warmup + i), args.steps) * args.steps
     nlaunch = max(10, args.steps)
     names = ["quantize_row", "quantize_transposed", "quantize_dual", "mm_fp8", "quantize_dynamic_row",
-             "quantize_dynamic_dual"]
+             "quantize_dynamic_dual", "mm_fp8_out_e4m3"]
+    C8_out = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    ring_c = fp8mi.new_ring(HIST, 1.0, dev)
     ws_dyn = torch.empty(fp8mi.DYNAMIC_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     launches = {
         "quantize_row": lambda i: fp8mi.fp8_quantize(xq[i % nq], fp8mi.E4M3, False, out=out_row, ring=rings[0],
@@ -238,6 +240,9 @@ def main():
         "quantize_dynamic_dual": lambda i: fp8mi.fp8_quantize_dynamic(xq[i % nq], fp8mi.E4M3, 2, out_row=out_row2,
                                                                       out_t=out_t2, scale_inv_out=sinv[2:3],
                                                                       workspace=ws_dyn),
+        # FP8-out GEMM: the quantizing epilogue with the output's ring fold
+        "mm_fp8_out_e4m3": lambda i: fp8mi.fp8_mm_ex(A[i % nm], B[i % nm], fp8mi.E4M3, fp8mi.E4M3, sa, sb, bias,
+                                                     out=C8_out, out_fmt=fp8mi.E4M3, out_ring=ring_c),
     }
     us = [timed(launches[nme], nlaunch) * 1e3 for nme in names]
     qbytes = {"quantize_row": R * C * 3, "quantize_transposed": R * C * 3, "quantize_dual": R * C * 4,
@@ -246,7 +251,7 @@ def main():
     mm_tflops = flops / (us[3] * 1e-6) / 1e12
     quant = {}
     for i, nme in enumerate(names):
-        if nme == "mm_fp8":
+        if nme.startswith("mm_fp8"):
             continue
         gbs = qbytes[nme] / (us[i] * 1e-6) / 1e9
         quant[nme] = {"us_per_launch": round(float(us[i]), 3), "GBps": round(gbs, 1),
@@ -286,6 +291,9 @@ def main():
                               "unit": "GB/s", "frac": quant["quantize_dual"]["frac_hbm_peak"], "traffic": None,
                               "kernel": "quantize_dual"},
         "quantize": quant,
+        "mm_fp8_out_e4m3": {"us_per_launch": round(float(us[names.index("mm_fp8_out_e4m3")]), 3),
+                            "TFLOPs": round(flops / (us[names.index("mm_fp8_out_e4m3")] * 1e-6) / 1e12, 1),
+                            "workload": "4096^3 E4M3 + fp32 bias -> E4M3 codes, ring scale + amax fold (H=16)"},
     }
     traffic = counter_traffic()
     if traffic:

@@ -14,10 +14,11 @@ import torch
 from ._lib import lib
 
 __all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual", "fp8_quantize_dual_bias_grad",
-           "fp8_quantize_dynamic", "DYNAMIC_WORKSPACE_BYTES", "fp8_amax_fold", "fp8_mm", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
+           "fp8_quantize_dynamic", "DYNAMIC_WORKSPACE_BYTES", "fp8_amax_fold", "fp8_mm", "fp8_mm_ex", "FP8_E4M3", "FP8_E5M2", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
 
 E4M3, E5M2 = 0, 1
 F32, F16, BF16 = 0, 1, 2
+FP8_E4M3, FP8_E5M2 = 3, 4  # fp8 storage types (fp8 bias / fp8 GEMM output of fp8_mm_ex)
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
@@ -219,6 +220,25 @@ def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_inv
            out: torch.Tensor | None = None) -> torch.Tensor:
     """C = bf16(A B^T * sa * sb + bias) for fp8 codes A [(batch,) M, K] and
     B [(batch,) N, K]; a size-1 (or stride-0) batch dimension broadcasts."""
+    return _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, None, None, out, None, ex=False)
+
+
+def fp8_mm_ex(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_inv: torch.Tensor | None = None,
+              b_scale_inv: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+              bias_fmt=None, bias_scale: torch.Tensor | None = None, out: torch.Tensor | None = None,
+              out_fmt=None, out_scale: torch.Tensor | None = None, out_ring: torch.Tensor | None = None,
+              out_scale_inv: torch.Tensor | None = None, out_amax: torch.Tensor | None = None) -> torch.Tensor:
+    """fp8_mm with an fp8-stored bias (codes `bias` of format `bias_fmt`,
+    dequantized by `bias_scale`) and/or a quantizing epilogue: with `out_fmt`
+    (E4M3 / E5M2) the output is fp8 codes quantized with `out_scale` or the
+    ring `out_ring` (which then folds the output's amax); `out_scale_inv` and
+    `out_amax` receive 1/s and amax."""
+    return _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_scale, out, out_fmt,
+                    out_scale, out_ring, out_scale_inv, out_amax)
+
+
+def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_scale, out, out_fmt,
+             out_scale=None, out_ring=None, out_scale_inv=None, out_amax=None, ex=True):
     a, b = _as_codes(a), _as_codes(b)
     a3 = a if a.dim() == 3 else a.unsqueeze(0)
     b3 = b if b.dim() == 3 else b.unsqueeze(0)
@@ -236,15 +256,30 @@ def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_inv
     sb = 0 if b3.shape[0] == 1 else b3.stride(0)
     lda = a3.stride(1) if M > 1 else K
     ldb = b3.stride(1) if N > 1 else K
+    c_dt = BF16 if out_fmt is None else FP8_E4M3 + _fmt(out_fmt)
     if out is None:
         shape = (batch, M, N) if (a.dim() == 3 or b.dim() == 3) else (M, N)
-        out = torch.empty(shape, dtype=torch.bfloat16, device=a.device)
+        out = torch.empty(shape, dtype=torch.bfloat16 if c_dt == BF16 else torch.uint8, device=a.device)
+    if c_dt != BF16:
+        out = _as_codes(out)
     c3 = out if out.dim() == 3 else out.unsqueeze(0)
     ldc = c3.stride(1) if M > 1 else N
     sc = c3.stride(0) if batch > 1 else M * ldc
-    bias_dt = _DT[bias.dtype] if bias is not None else 0
-    _check(lib().fp8_mm(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
-                        _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(out), ldc, sc, _stream(a)))
+    if bias is None:
+        bias_dt = 0
+    elif bias_fmt is not None:
+        bias, bias_dt = _as_codes(bias), FP8_E4M3 + _fmt(bias_fmt)
+    else:
+        bias_dt = _DT[bias.dtype]
+    if not ex:
+        _check(lib().fp8_mm(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
+                            _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(out), ldc, sc,
+                            _stream(a)))
+        return out
+    rp, h = _ring_args(out_ring)
+    _check(lib().fp8_mm_ex(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
+                           _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(bias_scale), _ptr(out),
+                           c_dt, ldc, sc, _ptr(out_scale), rp, h, _ptr(out_scale_inv), _ptr(out_amax), _stream(a)))
     return out
 
 

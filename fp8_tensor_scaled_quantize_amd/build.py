@@ -1,18 +1,24 @@
-"""Build libfp8mi.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc."""
+"""Build libfp8mi.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Every source compiles to its own object in parallel (the kernel template
+instantiations dominate the build time), then one link makes the library.
+"""
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["abi.hip", "quantize.hip", "mm_fp8.hip", "grad_bias.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "mm_fp8.hip", "mm_fp8_q8.hip", "grad_bias.hip"]
 LIB = os.path.join(PKG, "libfp8mi.so")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-fvisibility=hidden",
     # no hand-written or compiler-formed packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -20,20 +26,44 @@ HIPCC_FLAGS = [
 ]
 
 
+def _filter(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if "is not a recognized feature" not in l)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source into libfp8mi.so (always recompiles)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines() if "is not a recognized feature" not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    tmpdir = tempfile.mkdtemp(prefix="fp8mi_build_")
+    try:
+        procs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                     text=True)))
+        objs, errors = [], []
+        for src, obj, pr in procs:
+            _, err = pr.communicate()
+            err = _filter(err)
+            if pr.returncode != 0:
+                errors.append(f"{src}: hipcc failed ({pr.returncode}):\n{err}")
+            elif verbose and err.strip():
+                print(err, file=sys.stderr)
+            objs.append(obj)
+        if errors:
+            raise RuntimeError("\n".join(errors))
+        tmp = LIB + ".tmp"
+        cmd = [hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed ({r.returncode}):\n{_filter(r.stderr)}")
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

@@ -192,17 +192,44 @@ fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const float* amax, 
   return from_hip(launch_amax_fold(ring, hist_len, amax, fmt, static_cast<hipStream_t>(stream)), "fold launch");
 }
 
-fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, const uint8_t* b, int fmt_b,
-                    int64_t ldb, int64_t stride_b, int64_t M, int64_t N, int64_t K, int64_t batch,
-                    const float* a_scale_inv, const float* b_scale_inv, const void* bias, int bias_dtype, void* c,
-                    int64_t ldc, int64_t stride_c, void* stream) {
+fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, const uint8_t* b, int fmt_b,
+                       int64_t ldb, int64_t stride_b, int64_t M, int64_t N, int64_t K, int64_t batch,
+                       const float* a_scale_inv, const float* b_scale_inv, const void* bias, int bias_dtype,
+                       const float* bias_scale, void* c, int c_dtype, int64_t ldc, int64_t stride_c,
+                       const float* c_scale, uint32_t* c_ring, int32_t c_hist_len, float* c_scale_inv_out,
+                       float* c_amax_out, void* stream) {
   if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b))
     return fail(FP8MI_ERR_ENUM, "fmt_a %d / fmt_b %d must be FP8MI_E4M3/FP8MI_E5M2", fmt_a, fmt_b);
-  if (bias && !valid_dtype(bias_dtype)) return fail(FP8MI_ERR_ENUM, "bias_dtype %d is not F32/F16/BF16", bias_dtype);
+  const bool fp8_bias = bias_dtype == FP8MI_FP8_E4M3 || bias_dtype == FP8MI_FP8_E5M2;
+  if (bias && !valid_dtype(bias_dtype) && !fp8_bias)
+    return fail(FP8MI_ERR_ENUM, "bias_dtype %d is not F32/F16/BF16/FP8_E4M3/FP8_E5M2", bias_dtype);
+  if (bias && fp8_bias && !bias_scale) return fail(FP8MI_ERR_NULL, "an fp8 bias needs bias_scale");
+  if (bias_scale && !(bias && fp8_bias))
+    return fail(FP8MI_ERR_ARG, "bias_scale is only for an fp8-stored bias (null scale = raw bias)");
+  const bool fp8_out = c_dtype == FP8MI_FP8_E4M3 || c_dtype == FP8MI_FP8_E5M2;
+  if (c_dtype != FP8MI_BF16 && !fp8_out) return fail(FP8MI_ERR_ENUM, "c_dtype %d is not BF16/FP8_E4M3/FP8_E5M2", c_dtype);
+  if (fp8_out) {
+    fp8mi_status s = check_scale_ring(c_scale, c_ring, c_hist_len);
+    if (s != FP8MI_OK) return s;
+  } else if (c_scale || c_ring || c_scale_inv_out || c_amax_out) {
+    return fail(FP8MI_ERR_ARG, "output scale, ring, scale_inv and amax are for an fp8 output only");
+  }
   if (M < 0 || N < 0 || K < 0 || batch < 0)
     return fail(FP8MI_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld batch=%lld", (long long)M, (long long)N,
                 (long long)K, (long long)batch);
-  if (M == 0 || N == 0 || batch == 0) return FP8MI_OK;
+  if ((reinterpret_cast<uintptr_t>(c_scale) | reinterpret_cast<uintptr_t>(c_scale_inv_out) |
+       reinterpret_cast<uintptr_t>(c_amax_out) | reinterpret_cast<uintptr_t>(bias_scale)) & 3u)
+    return fail(FP8MI_ERR_ARG, "fp32 scalars must be 4-byte aligned");
+  MmArgs p;
+  p.M = M; p.N = N; p.K = K; p.batch = batch;
+  p.out_fmt = fp8_out ? (c_dtype == FP8MI_FP8_E4M3 ? (int)FP8MI_E4M3 : (int)FP8MI_E5M2) : -1;
+  p.c_scale = c_scale; p.c_ring = c_ring; p.c_H = c_hist_len;
+  p.c_scale_inv_out = c_scale_inv_out; p.c_amax_out = c_amax_out;
+  if (M == 0 || N == 0 || batch == 0) {
+    // nothing to compute; an fp8 output still completes its scale bookkeeping
+    if (!fp8_out) return FP8MI_OK;
+    return from_hip(launch_mm(p, fmt_a, fmt_b, static_cast<hipStream_t>(stream)), "mm launch");
+  }
   if (!c) return fail(FP8MI_ERR_NULL, "c is NULL");
   if (K > 0 && (!a || !b)) return fail(FP8MI_ERR_NULL, "a or b is NULL");
   if (ldc < N) return fail(FP8MI_ERR_SHAPE, "ldc %lld < N %lld", (long long)ldc, (long long)N);
@@ -212,8 +239,8 @@ fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, 
   if (batch > 1 && stride_c < M * ldc)
     return fail(FP8MI_ERR_STRIDE, "stride_c %lld < M*ldc %lld: batches would overlap", (long long)stride_c,
                 (long long)(M * ldc));
-  if (reinterpret_cast<uintptr_t>(c) & 1u) return fail(FP8MI_ERR_ARG, "c must be 2-byte aligned");
-  if (bias && (reinterpret_cast<uintptr_t>(bias) % dtype_bytes(bias_dtype)))
+  if (!fp8_out && (reinterpret_cast<uintptr_t>(c) & 1u)) return fail(FP8MI_ERR_ARG, "c must be 2-byte aligned");
+  if (bias && !fp8_bias && (reinterpret_cast<uintptr_t>(bias) % dtype_bytes(bias_dtype)))
     return fail(FP8MI_ERR_ARG, "bias not aligned to its element size");
   if (K > 0) {
     if ((K % 16) || (lda % 16) || (ldb % 16))
@@ -226,9 +253,22 @@ fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, 
   }
   if ((M + 63) / 64 > 65535 || batch > 65535)
     return fail(FP8MI_ERR_UNSUPPORTED, "M=%lld / batch=%lld beyond the launch grid", (long long)M, (long long)batch);
-  MmArgs p{a, b, lda, ldb, stride_a, stride_b, M, N, K, batch, a_scale_inv, b_scale_inv,
-           bias, bias ? bias_dtype : -1, static_cast<uint16_t*>(c), ldc, stride_c};
+  p.a = a; p.b = b; p.lda = lda; p.ldb = ldb; p.stride_a = stride_a; p.stride_b = stride_b;
+  p.a_scale_inv = a_scale_inv; p.b_scale_inv = b_scale_inv;
+  p.bias = bias; p.bias_dtype = bias ? bias_dtype : -1; p.bias_scale = bias_scale;
+  p.c = c; p.ldc = ldc; p.stride_c = stride_c;
+  if (fp8_out && !(p.a_extent_from(0) < (1ll << 31) && p.b_extent_from(0) < (1ll << 31) && K < (1ll << 30)))
+    return fail(FP8MI_ERR_UNSUPPORTED, "an fp8 output needs operand extents below 2^31 bytes");
   return from_hip(launch_mm(p, fmt_a, fmt_b, static_cast<hipStream_t>(stream)), "mm launch");
+}
+
+fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, const uint8_t* b, int fmt_b,
+                    int64_t ldb, int64_t stride_b, int64_t M, int64_t N, int64_t K, int64_t batch,
+                    const float* a_scale_inv, const float* b_scale_inv, const void* bias, int bias_dtype, void* c,
+                    int64_t ldc, int64_t stride_c, void* stream) {
+  if (bias && !valid_dtype(bias_dtype)) return fail(FP8MI_ERR_ENUM, "bias_dtype %d is not F32/F16/BF16", bias_dtype);
+  return fp8_mm_ex(a, fmt_a, lda, stride_a, b, fmt_b, ldb, stride_b, M, N, K, batch, a_scale_inv, b_scale_inv, bias,
+                   bias_dtype, nullptr, c, FP8MI_BF16, ldc, stride_c, nullptr, nullptr, 0, nullptr, nullptr, stream);
 }
 
 size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols) {

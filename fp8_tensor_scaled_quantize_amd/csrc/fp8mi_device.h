@@ -7,7 +7,7 @@
 namespace fp8mi {
 
 enum Fmt : int { kE4M3 = 0, kE5M2 = 1 };
-enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFp8E4M3 = 3, kFp8E5M2 = 4 };
 
 template <int FMT> struct FmtTraits;
 // OCP E4M3FN: largest finite 448 (S.1111.110); E5M2: 57344 (S.11110.11).

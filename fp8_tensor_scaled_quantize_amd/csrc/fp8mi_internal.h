@@ -34,16 +34,24 @@ hipError_t launch_quantize_dynamic(const void* x, int dt, int64_t rows, int64_t 
 hipError_t launch_amax_fold(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st);
 
 struct MmArgs {
-  const uint8_t* a;
-  const uint8_t* b;
-  int64_t lda, ldb, stride_a, stride_b;
-  int64_t M, N, K, batch;
-  const float* a_scale_inv;
-  const float* b_scale_inv;
-  const void* bias;
-  int bias_dtype;  // -1: no bias
-  uint16_t* c;
-  int64_t ldc, stride_c;
+  const uint8_t* a = nullptr;
+  const uint8_t* b = nullptr;
+  int64_t lda = 0, ldb = 0, stride_a = 0, stride_b = 0;
+  int64_t M = 0, N = 0, K = 0, batch = 0;
+  const float* a_scale_inv = nullptr;
+  const float* b_scale_inv = nullptr;
+  const void* bias = nullptr;
+  int bias_dtype = -1;                // -1: no bias; kF32 / kF16 / kBF16; kFp8E4M3 / kFp8E5M2 codes
+  const float* bias_scale = nullptr;  // dequantisation multiplier of an fp8 bias
+  void* c = nullptr;                  // bf16 (out_fmt < 0) or fp8 codes (out_fmt = kE4M3 / kE5M2)
+  int64_t ldc = 0, stride_c = 0;      // elements
+  int out_fmt = -1;
+  // fp8 output: scale from c_scale or the ring c_ring (history c_H); optional 1/s and amax outputs
+  const float* c_scale = nullptr;
+  uint32_t* c_ring = nullptr;
+  int c_H = 0;
+  float* c_scale_inv_out = nullptr;
+  float* c_amax_out = nullptr;
 
   // Bytes of one batch's A (B) from row r on: the last row ends at K.
   __host__ __device__ int64_t a_extent_from(int64_t r) const { return r < M ? (M - 1 - r) * lda + K : 0; }
@@ -51,6 +59,10 @@ struct MmArgs {
 };
 
 hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+// fp8-output GEMM (p.out_fmt >= 0, operand extents below 2^31 bytes).
+hipError_t launch_mm_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+// One fp32 word set to 0 on the stream (a fill kernel, capturable).
+hipError_t launch_zero_word(float* p, hipStream_t st);
 
 // Bytes of fp64 workspace the bias gradient needs (per-chunk column sums).
 int64_t grad_bias_workspace_bytes(int64_t rows, int64_t cols);

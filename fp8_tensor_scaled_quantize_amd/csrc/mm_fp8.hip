@@ -1,6 +1,8 @@
 // Per-tensor-scaled fp8 GEMM on CDNA4 MFMA (gfx950), NT operands, fp32
 // accumulation, fused fp32 bias, one bf16 rounding of the output, batched
-// through grid.z with optional stride-0 broadcast.
+// through grid.z with optional stride-0 broadcast.  The kernel template lives
+// in mm_fp8_kernel.h; this unit holds the bf16-output instantiations and the
+// dispatch, mm_fp8_q8.hip the fp8-output ones (the quantizing epilogue).
 //
 // log:tests/extension -- the commit fusing the linear bias into the GEMM
 // epilogue (added in fp32 before the single bf16 rounding, guarded N tails,
@@ -17,53 +19,9 @@
 // and writes 8 contiguous bytes of bf16.  LDS tiles hold 128 K-bytes per row,
 // 16-byte chunks XOR-swizzled (see swz) so that the 16 rows one MFMA
 // fragment reads spread over the banks.
-#include "fp8mi_device.h"
-#include "fp8mi_internal.h"
-
-#include <cstdlib>
+#include "mm_fp8_kernel.h"
 
 namespace fp8mi {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-constexpr int kBK = 128;
-constexpr int kMmThreads = 256;
-
-// LDS tiles: rows of kBK = 128 bytes; the 16-byte chunk c of row r sits at
-// chunk position c ^ swz(r).  gfx950 serves a ds_read_b128 16 lanes per cycle
-// from 64 four-byte banks, each half-wave in two cycles split by the parity
-// of lane bits 2..4 (measured with the LDS bank-conflict counter).  In an
-// MFMA fragment read lane l reads row l%16, chunk 2(l/16) + h; swz(r) =
-// ((r >> 1) & 1) | (r & 4) puts every such cycle's 16 reads on 16 distinct
-// 16-byte bank groups (row parity picks the 128-byte half, the chunk
-// position the group within it).
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 1) | (row & 4); }
-
-__device__ __forceinline__ v8i lds_frag(const uint8_t* S, int row, int g) {
-  const int sw = swz(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(S + row * kBK + (((2 * g) ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(S + row * kBK + (((2 * g + 1) ^ sw) << 4));
-  v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
-}
-
-__device__ __forceinline__ float load_bias(const void* bias, int dt, int64_t j) {
-  if (dt == kF32) return static_cast<const float*>(bias)[j];
-  if (dt == kBF16) return bf16_to_f32(static_cast<const uint16_t*>(bias)[j]);
-  return f16_to_f32(static_cast<const uint16_t*>(bias)[j]);
-}
-
-template <int FA, int FB>
-__device__ __forceinline__ v4f mfma_nt(const v8i& bfrag, const v8i& afrag, const v4f& c) {
-  // first operand: B rows (format FB -> cbsz), second: A rows (format FA -> blgp).
-  // Zero block-scale operands make the compiler emit the unscaled
-  // v_mfma_f32_16x16x128_f8f6f4 (no scale prefix; 2-3% faster in an MFMA-bound
-  // loop on MI355X, identical results).
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfrag, afrag, c, FB, FA, 0, 0, 0, 0);
-}
 
 template <int BM, int BN, int FA, int FB>
 __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
@@ -145,7 +103,8 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
   const float sa = p.a_scale_inv ? *p.a_scale_inv : 1.0f;
   const float sb = p.b_scale_inv ? *p.b_scale_inv : 1.0f;
   const float sab = sa * sb;
-  uint16_t* C = p.c + bz * p.stride_c;
+  const float bscale = p.bias_scale ? *p.bias_scale : 1.0f;
+  uint16_t* C = static_cast<uint16_t*>(p.c) + bz * p.stride_c;
   const int mr = lane & 15, ng = lane >> 4;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
@@ -158,7 +117,7 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
       uint32_t h[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float bv = (p.bias && gn + r < p.N) ? load_bias(p.bias, p.bias_dtype, gn + r) : 0.0f;
+        const float bv = (p.bias && gn + r < p.N) ? load_bias(p, gn + r, bscale) : 0.0f;
         h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bv));
       }
       uint16_t* dst = C + gm * p.ldc + gn;
@@ -173,262 +132,10 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
   }
 }
 
-// ===========================================================================
-// Large-tile kernel: 256 x 256 block tile, 8 waves (2 along M x 4 along N),
-// each wave 128 x 64 = 8 x 4 MFMA tiles (128 fp32 accumulators per lane).
-// K advances 128 bytes per step through two LDS stages (2 x 64 KiB).  The
-// operands go from HBM/L2 straight into LDS (buffer_load_dwordx4 ... lds):
-// each load instruction fills 1 KiB = 8 tile rows, lane l writing 16 bytes at
-// l * 16, so lane l fetches the 16-byte chunk that the XOR swizzle places
-// there (row r0 + l/8, chunk (l%8) ^ (l/8)).  The loads of step k+1 are in
-// flight while step k's MFMAs run; one wait + barrier per step.  Rows past
-// the matrix edge and chunks past K read as zero: their buffer offsets lie
-// beyond the resource's byte count.
-// Workgroups are renumbered so that the ones a single XCD runs (the hardware
-// deals workgroup ids round-robin over the 8 XCDs) cover a compact block of
-// tiles -- group_m tile rows by consecutive tile columns -- and share their
-// A and B panels in that XCD's L2.
-// ===========================================================================
-constexpr int kBigThreads = 512;
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over `bytes` bytes from `base` (stride 0, dword3 as for
-// all gfx9 raw buffers); reads at offsets >= bytes return zero.
-__device__ __forceinline__ v4i buffer_rsrc(const void* base, int bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  v4i r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xFFFF);
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// 16 bytes per lane from a raw buffer straight into LDS at lds + 16 * lane.
-// Written as asm so that the compiler's wait-count pass does not treat the
-// LDS write as aliasing the current stage's ds_reads (it would otherwise wait
-// for this prefetch before every read); the kernel waits for it explicitly
-// (s_waitcnt vmcnt(0) + barrier) before the stage is read.  The asm has no
-// register outputs; M0 is saved and restored around it.
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
-
-__device__ __forceinline__ void tile_coords(int64_t wg, int64_t tiles_m, int64_t tiles_n, int group_m,
-                                            int64_t& tm, int64_t& tn) {
-  const int64_t T = tiles_m * tiles_n;
-  const int64_t full = (T / 8) * 8;
-  int64_t id = wg;
-  if (wg < full) id = (wg % 8) * (full / 8) + wg / 8;  // same-XCD workgroups get consecutive ids
-  const int64_t per_group = (int64_t)group_m * tiles_n;
-  const int64_t g = id / per_group, r = id % per_group;
-  const int64_t rows_here = (tiles_m - g * group_m) < group_m ? (tiles_m - g * group_m) : group_m;
-  tm = g * group_m + r % rows_here;
-  tn = r / rows_here;
-}
-
-template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma(MmArgs p, int64_t tiles_m,
-                                                                                 int64_t tiles_n, int group_m) {
-  constexpr int NWAVES = WAVES_M * WAVES_N;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int TI = WM / 16, TJ = WN / 16;
-  constexpr int STAGE = (BM + BN) * kBK;      // bytes per LDS stage
-  constexpr int LA = BM / 8 / NWAVES;         // 1 KiB load instructions per wave for A
-  constexpr int LB = BN / 8 / NWAVES;         // ... and for B
-  static_assert(LA >= 1 && LB >= 1 && LA * 8 * NWAVES == BM && LB * 8 * NWAVES == BN, "tile / wave mismatch");
-  static_assert(TI >= 1 && TJ >= 1, "wave tile below one MFMA tile");
-  constexpr int CROW = BN + 8;                // bf16 per LDS row of the staged C tile (16 B pad)
-  constexpr int SMEM = 2 * STAGE > BM * CROW * 2 ? 2 * STAGE : BM * CROW * 2;
-  __shared__ __align__(16) uint8_t smem[SMEM];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
-  const int64_t bz = blockIdx.z;
-  int64_t tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int ext_a = (int)p.a_extent_from(m0), ext_b = (int)p.b_extent_from(n0);
-  const v4i rsa = buffer_rsrc(p.a + bz * p.stride_a + m0 * p.lda, ext_a);
-  const v4i rsb = buffer_rsrc(p.b + bz * p.stride_b + n0 * p.ldb, ext_b);
-  // Lane l of a 1 KiB load fills LDS row r0 + l/8 (r0 a multiple of 8) at
-  // chunk position l%8, so it fetches logical chunk (l%8) ^ swz(l/8).
-  const int lr = lane >> 3, lc = (lane & 7) ^ swz(lr);
-  // unsigned: offsets of rows past the edge may wrap; those rows' outputs are never stored
-  const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
-  const uint32_t va = lr * lda + 16 * lc, vb = lr * ldb + 16 * lc;
-  const int K = (int)p.K;
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
-
-  // Issue one stage of loads (this wave's 4 + 4 instructions).
-  // One stage of loads: this wave's LA instructions for A rows
-  // (wid * LA + q) * 8 .. + 7 and LB for B rows (wid * LB + q) * 8 .. + 7.
-  // The raw-buffer range check covers voffset + soffset (measured on MI355X):
-  // a row past the matrix edge starts at or beyond the extent and a chunk at
-  // or past K gets the extent itself as its voffset, so both read as zero.
-  auto issue_all = [&](int stage, int k0) {
-    const bool past = k0 + 16 * lc >= K;  // K tail: chunks at or past K read as zero
-    const uint32_t as = smem_lds + stage * STAGE, bs = as + BM * kBK;
-#pragma unroll
-    for (int q = 0; q < (LA > LB ? LA : LB); ++q) {
-      if (q < LA) {
-        const int r0 = (wid * LA + q) * 8;
-        dma16(rsa, as + r0 * kBK, past ? ext_a : (int)(va + (uint32_t)r0 * lda), k0);
-      }
-      if (q < LB) {
-        const int r0 = (wid * LB + q) * 8;
-        dma16(rsb, bs + r0 * kBK, past ? ext_b : (int)(vb + (uint32_t)r0 * ldb), k0);
-      }
-    }
-  };
-
-  v4f acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int nk = (K + kBK - 1) / kBK;
-  const int r16 = lane & 15, g = lane >> 4;
-  if (nk > 0) issue_all(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* As = smem + (kt & 1) * STAGE;
-    const uint8_t* Bs = As + BM * kBK;
-    if (kt + 1 < nk) issue_all((kt + 1) & 1, (kt + 1) * kBK);
-    v8i bfr[TJ];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) bfr[j] = lds_frag(Bs, wn * WN + 16 * j + r16, g);
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const v8i af = lds_frag(As, wm * WM + 16 * i + r16, g);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_nt<FA, FB>(bfr[j], af, acc[i][j]);
-    }
-    wait_vmem();
-    __syncthreads();
-  }
-
-  // Epilogue: y = acc * fl32(sa * sb) + bias[j], one bf16 rounding.
-  const float sa = p.a_scale_inv ? *p.a_scale_inv : 1.0f;
-  const float sb = p.b_scale_inv ? *p.b_scale_inv : 1.0f;
-  const float sab = sa * sb;
-  uint16_t* C = p.c + bz * p.stride_c;
-  const int ng = lane >> 4;
-  float bias_v[TJ][4];
-#pragma unroll
-  for (int j = 0; j < TJ; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng + r;
-      bias_v[j][r] = (p.bias && gn < p.N) ? load_bias(p.bias, p.bias_dtype, gn) : 0.0f;
-    }
-  // Interior tiles go out through LDS (the stages are free after the K loop):
-  // each lane parks its 4-column pieces in a [256][256 + 8] bf16 tile, then
-  // every wave stores whole 512-byte rows with 16-byte lanes.
-  const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && (p.ldc % 8) == 0 &&
-                        ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
-  if (interior) {
-    uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int lm = wm * WM + 16 * i + r16;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bias_v[j][r]));
-        *reinterpret_cast<uint2*>(Cs + lm * CROW + wn * WN + 16 * j + 4 * ng) =
-            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      }
-    }
-    __syncthreads();
-    // BN / 8 lanes x 16 bytes per row; a wave stores RPW rows per step (lanes
-    // past RPW * LPR idle when BN / 8 does not divide 64, e.g. BN = 192)
-    constexpr int LPR = BN / 8, RPW = 64 / LPR;
-    const int sub = lane / LPR, cl = lane % LPR;
-#pragma unroll 4
-    for (int rr = wid * RPW + sub; sub < RPW && rr < BM; rr += RPW * NWAVES) {
-      const uint4 v = *reinterpret_cast<const uint4*>(Cs + rr * CROW + 8 * cl);
-      *reinterpret_cast<uint4*>(C + (m0 + rr) * p.ldc + n0 + 8 * cl) = v;
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int64_t gm = m0 + wm * WM + 16 * i + r16;
-    if (gm >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng;
-      if (gn >= p.N) continue;
-      uint32_t h[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bias_v[j][r]));
-      uint16_t* dst = C + gm * p.ldc + gn;
-      if (gn + 4 <= p.N && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (gn + r < p.N) dst[r] = (uint16_t)h[r];
-      }
-    }
-  }
-}
-
-// Tile dispatch (measured on MI355X over the shapes of the test configs):
-// the 8-wave big-tile kernels whenever their tiles (x batch) cover at least
-// 60% of the CUs -- one round of big tiles beats several rounds of small ones
-// even with part of the chip idle -- choosing 256 x 192 over 256 x 256 when it
-// needs less work per CU (rounds of workgroups x tile width: the backward
-// GEMMs of the 1536-wide linear get 256 and 216 workgroups instead of 192 and
-// 162, 10-11% faster), and the 64x128 / 4-wave kernel (two per CU) below 60%.
-// 128x128 is reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128
-// kernel remains for operands whose byte extent does not fit a 32-bit buffer
-// offset.
-template <int FA, int FB, int BM, int BN, int WM_, int WN_, int MINB>
-static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
-  const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
-  hipLaunchKernelGGL((mm_fp8_dma<FA, FB, BM, BN, WM_, WN_, MINB>), grid, dim3(64 * WM_ * WN_), 0, st, p, tiles_m,
-                     tiles_n, 4);
-  return hipGetLastError();
-}
-
-static int pick_tile(const MmArgs& p, int ncu) {
-  static const int forced = [] { const char* e = getenv("FP8MI_MM_TILE"); return e ? atoi(e) : -1; }();
-  if (forced >= 0 && forced < 4) return forced;
-  const int64_t tm = (p.M + 255) / 256;
-  const int64_t t256 = tm * ((p.N + 255) / 256) * p.batch, t192 = tm * ((p.N + 191) / 192) * p.batch;
-  if (10 * (t256 > t192 ? t256 : t192) < 6 * (int64_t)ncu) return 2;
-  // per-CU work of the big-tile family: rounds of workgroups x tile width
-  const int64_t cost256 = ((t256 + ncu - 1) / ncu) * 256, cost192 = ((t192 + ncu - 1) / ncu) * 192;
-  return cost192 < cost256 ? 3 : 0;
-}
-
+// Large operands (byte extents beyond a 32-bit buffer offset) take the
+// 128x128 plain-load kernel; everything else the LDS-DMA big-tile family.
 template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStream_t st) {
-  // buffer offsets are 32-bit: extent + largest soffset must stay below 2^32
-  const bool fits31 = p.a_extent_from(0) < (1ll << 31) && p.b_extent_from(0) < (1ll << 31) && p.K < (1ll << 30);
-  if (fits31) {
-    switch (pick_tile(p, device_cu_count())) {
-      case 0: return launch_dma<FA, FB, 256, 256, 2, 4, 1>(p, st);
-      case 3: return launch_dma<FA, FB, 256, 192, 2, 4, 1>(p, st);
-      case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2>(p, st);
-      default: return launch_dma<FA, FB, 64, 128, 1, 4, 2>(p, st);
-    }
-  }
+  if (mm_fits31(p)) return launch_dma_family<FA, FB, -1>(p, st);
   constexpr int BM = 128, BN = 128;
   const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.batch);
   hipLaunchKernelGGL((mm_fp8_tile<BM, BN, FA, FB>), grid, dim3(kMmThreads), 0, st, p);
@@ -436,6 +143,7 @@ template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStre
 }
 
 hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st) {
+  if (p.out_fmt >= 0) return launch_mm_q8(p, fmt_a, fmt_b, st);
   if (fmt_a == kE4M3 && fmt_b == kE4M3) return launch_fmts<kE4M3, kE4M3>(p, st);
   if (fmt_a == kE5M2 && fmt_b == kE4M3) return launch_fmts<kE5M2, kE4M3>(p, st);
   if (fmt_a == kE4M3 && fmt_b == kE5M2) return launch_fmts<kE4M3, kE5M2>(p, st);

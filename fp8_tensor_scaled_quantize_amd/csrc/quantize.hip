@@ -660,6 +660,11 @@ __global__ void zero_word_kernel(float* p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0.0f;
 }
 
+hipError_t launch_zero_word(float* p, hipStream_t st) {
+  hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
 // ===========================================================================
 // Current scaling, first pass.  Every workgroup writes the NaN-free max |x| of
 // its share of the input to parts[blockIdx.x] as fp32 bits; the quantize pass

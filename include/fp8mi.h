@@ -72,7 +72,13 @@ typedef enum {
 } fp8mi_status;
 
 typedef enum { FP8MI_E4M3 = 0, FP8MI_E5M2 = 1 } fp8mi_format;
-typedef enum { FP8MI_F32 = 0, FP8MI_F16 = 1, FP8MI_BF16 = 2 } fp8mi_dtype;
+typedef enum {
+  FP8MI_F32 = 0,
+  FP8MI_F16 = 1,
+  FP8MI_BF16 = 2,
+  FP8MI_FP8_E4M3 = 3, /* fp8 codes, one byte per element (bias / GEMM output of fp8_mm_ex) */
+  FP8MI_FP8_E5M2 = 4
+} fp8mi_dtype;
 
 /* Largest history window a ring may have, and the ring size in words. */
 #define FP8MI_MAX_HIST 4096
@@ -188,6 +194,42 @@ FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t 
                     const float* a_scale_inv, const float* b_scale_inv,
                     const void* bias, int bias_dtype,
                     void* c, int64_t ldc, int64_t stride_c, void* stream);
+
+/*
+ * fp8_mm_ex -- fp8_mm with an fp8-stored bias and an optional quantizing
+ * epilogue (FP8-in / FP8-out GEMM; log:tests/extension, the commit adding the
+ * FP8-in/FP8-out GEMM op and the commit giving the bias a bias_scale slot:
+ * no scale = a raw bias, a scale = fp8 storage dequantized in the epilogue
+ * after the operand scaling and before any output quantization).
+ *   y[b,i,j] = fl32( sum_k dec(A) dec(B) ) * fl32(sa * sb) + bias_j   (fp32)
+ *   bias_j     bias_dtype FP8MI_F32 / F16 / BF16: the value, widened exactly
+ *              (bias_scale must be NULL); FP8MI_FP8_E4M3 / E5M2: fl32(dec(code)
+ *              * *bias_scale), bias_scale a device fp32 (required).
+ *   c_dtype    FP8MI_BF16: C = bf16(y), exactly fp8_mm (c_scale, c_ring,
+ *              c_scale_inv_out and c_amax_out must be NULL).
+ *              FP8MI_FP8_E4M3 / E5M2: C holds codes enc(fl32(y * s_c)), one byte
+ *              per element, C(b,i,j) at c[b * stride_c + i * ldc + j] (element
+ *              strides); the output is quantized like an fp32 tensor by
+ *              fp8_quantize: s_c = *c_scale, or the ring c_ring's current scale
+ *              (exactly one of the two; ring layout and fold as fp8_quantize),
+ *              amax = max |y| over every output of every batch (NaN ignored),
+ *              one fold of it into the ring, c_scale_inv_out = 1 / s_c and
+ *              c_amax_out = amax (both optional).  Operand extents must stay
+ *              below 2^31 bytes (else FP8MI_ERR_UNSUPPORTED).
+ * Other arguments and requirements as fp8_mm.  M, N or batch 0 writes no
+ * codes; an fp8 output then still folds amax 0 into its ring (or writes
+ * 1 / s_c and amax 0).  y is fp32, so its accumulation error is that of
+ * fp8_mm before the bf16 rounding; an output near a code boundary may take
+ * the neighbouring code.
+ */
+FP8MI_API fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a,
+                                 const uint8_t* b, int fmt_b, int64_t ldb, int64_t stride_b,
+                                 int64_t M, int64_t N, int64_t K, int64_t batch,
+                                 const float* a_scale_inv, const float* b_scale_inv,
+                                 const void* bias, int bias_dtype, const float* bias_scale,
+                                 void* c, int c_dtype, int64_t ldc, int64_t stride_c,
+                                 const float* c_scale, uint32_t* c_ring, int32_t c_hist_len,
+                                 float* c_scale_inv_out, float* c_amax_out, void* stream);
 
 /*
  * fp8_quantize_dual_bias_grad -- fp8_quantize_dual of an output gradient

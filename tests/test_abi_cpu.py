@@ -200,3 +200,32 @@ def test_quantize_dynamic_rejects(L):
     assert call(ws=None, rows=0) == NULL
     assert call(wsb=W - 4) == ARG            # workspace too small
     assert call(ws=FAKE + 2) == ARG          # workspace not 4-byte aligned
+
+
+def test_mm_ex_rejects(L):
+    f = L.fp8_mm_ex
+
+    def call(a=FAKE, fa=0, lda=32, sa=0, b=FAKE, fb=0, ldb=32, sb=0, M=4, N=4, K=32, batch=1, bias=None, bdt=0,
+             bsc=None, c=FAKE, cdt=2, ldc=4, sc=16, cscale=None, cring=None, h=0, sinv=None, amax=None):
+        return f(a, fa, lda, sa, b, fb, ldb, sb, M, N, K, batch, None, None, bias, bdt, bsc, c, cdt, ldc, sc, cscale,
+                 cring, h, sinv, amax, None)
+
+    assert call(fa=2) == ENUM
+    assert call(cdt=0) == ENUM                        # fp32 output is not offered
+    assert call(cdt=5) == ENUM
+    assert call(bias=FAKE, bdt=9) == ENUM
+    assert call(bias=FAKE, bdt=3) == NULL             # fp8 bias without its scale
+    assert call(bias=FAKE, bdt=2, bsc=FAKE) == ARG    # a scale with a raw bias
+    assert call(bsc=FAKE) == ARG                      # a scale without a bias
+    assert call(cscale=FAKE) == ARG                   # output scale with a bf16 output
+    assert call(amax=FAKE) == ARG
+    assert call(cdt=3) == ARG                         # fp8 output: neither scale nor ring
+    assert call(cdt=3, cscale=FAKE, cring=FAKE, h=4) == ARG   # ... or both
+    assert call(cdt=4, cring=FAKE, h=0) == SHAPE      # ring with a bad history length
+    assert call(cdt=3, cscale=FAKE + 2) == ARG        # misaligned fp32 scalar
+    assert call(cdt=3, cscale=FAKE, M=-1) == SHAPE
+    assert call(cdt=3, cscale=FAKE, c=None) == NULL
+    assert call(cdt=3, cscale=FAKE, ldc=3) == SHAPE
+    assert call(cdt=3, cscale=FAKE, K=24, lda=24, ldb=24) == UNSUP
+    # the plain fp8_mm refuses an fp8 bias type (it has no bias scale)
+    assert L.fp8_mm(FAKE, 0, 32, 0, FAKE, 0, 32, 0, 4, 4, 32, 1, None, None, FAKE, 3, FAKE, 4, 16, None) == ENUM
