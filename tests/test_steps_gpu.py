@@ -19,7 +19,7 @@ import torch
 
 import oracle as O
 import synth
-from tests.gpu_util import DEV, as_bits, check, np_bf16_bits, np_codes, ring_state_words
+from tests.gpu_util import DEV, as_bits, check, np_bf16_bits, np_codes, ring_from_oracle, ring_state_words
 
 pytestmark = pytest.mark.gpu
 
@@ -239,3 +239,73 @@ def test_full_shape_dynamic_step():
               O.scale_inv(sg), O.scale_inv(sw), None, tag=f"dyn dX {t}")
         db_ref, db_mag = O.grad_bias(dy)
         assert np.array_equal(np_bf16_bits(db), db_ref), t
+
+
+def test_prequantized_weight_and_fp8_bias():
+    """w8 / b8, w8 / bf16 bias and the amax_w = 0 contract against an explicit
+    quantization reference: a layer over pre-quantized E4M3 weight codes skips
+    the weight quantize (its amax reads 0) and gives the outputs of the same
+    codes pushed through the oracle; an E5M2-stored bias is dequantized by its
+    scale in the epilogue."""
+    xs, w, b = tiny_inputs(2)
+    qw = O.quantize_dynamic(w, "bf16", O.E4M3)
+    bf = O.widen_to_f32(b, "bf16")
+    s_b = np.float32(O.FMT_MAX[O.E5M2]) / O.amax(bf)
+    b8 = O.encode(O.scaled_values(bf, s_b), O.E5M2)
+    sbi = O.scale_inv(s_b)
+    for bias_kind in ("b8", "bf16"):
+        if bias_kind == "b8":
+            layer = Fp8Linear.from_fp8_weight(torch.from_numpy(qw["codes"]).to(DEV),
+                                              torch.tensor([qw["scale_inv"]], dtype=torch.float32, device=DEV),
+                                              torch.from_numpy(b8).to(DEV), codes_t=torch.from_numpy(qw["codes_t"]).to(DEV),
+                                              bias_fmt=fp8mi.E5M2,
+                                              bias_scale=torch.tensor([sbi], dtype=torch.float32, device=DEV))
+            bias = O.dequant_bias(b8, O.E5M2, sbi).astype(np.float64)
+        else:
+            layer = Fp8Linear.from_fp8_weight(torch.from_numpy(qw["codes"]).to(DEV),
+                                              torch.tensor([qw["scale_inv"]], dtype=torch.float32, device=DEV), dev_bf16(b),
+                                              codes_t=torch.from_numpy(qw["codes_t"]).to(DEV))
+            bias = bf.astype(np.float64)
+        rx = O.seed_ring(4, xs[0], "bf16", O.E4M3)
+        layer.seed(dev_bf16(xs[0]))
+        for t in range(2):
+            ref_x = O.quantize(xs[t], "bf16", O.E4M3, ring=rx)
+            y = layer.forward(dev_bf16(xs[t]))
+            dx, dw, db = layer.backward(dev_bf16(synth.gaussian((64, 256), 1e-3, "bf16", 1, synth.T_DY, t)))
+            torch.cuda.synchronize()
+            amax = f32_words(layer.amax)
+            assert amax[1] == 0 and amax[0] == as_bits(ref_x["amax"]), (bias_kind, t)   # amax_w = 0
+            xq, wq = layer.last_codes
+            assert np.array_equal(np_codes(xq), ref_x["codes"]) and np.array_equal(np_codes(wq), qw["codes"])
+            check(np_bf16_bits(y), ref_x["codes"], O.E4M3, qw["codes"], O.E4M3, ref_x["scale_inv"], qw["scale_inv"],
+                  bias, tag=f"w8 {bias_kind} step {t}")
+            rx = ref_x["ring"]
+
+
+def test_fp8_out_layer_chain():
+    """Inference chaining: layer 1 returns E4M3 codes of Y from its quantizing
+    epilogue (output ring), layer 2 consumes them as x with their scale_inv --
+    no quantize between the layers -- against the oracle's mm_quantized then mm."""
+    x = synth.gaussian((64, 256), 1.0, "bf16", 3, synth.T_X, 0)
+    w1 = synth.gaussian((256, 256), 0.05, "bf16", 3, synth.T_W, 1)
+    w2 = synth.gaussian((128, 256), 0.05, "bf16", 3, synth.T_W, 2)
+    b2 = synth.gaussian((128,), 0.1, "bf16", 3, synth.T_BIAS, 2)
+    l1 = Fp8Linear(dev_bf16(w1), None, hist_len=4, dynamic=True)
+    l2 = Fp8Linear(dev_bf16(w2), dev_bf16(b2), hist_len=4, dynamic=True)
+    ry0 = O.Ring.new(4, 8.0)
+    l1.ring_y.copy_(ring_from_oracle(ry0))
+    y1, y1_sinv = l1.forward(dev_bf16(x), save_for_backward=False, out_fp8=True)
+    y2 = l2.forward(y1, save_for_backward=False, x_scale_inv=y1_sinv)
+    torch.cuda.synchronize()
+    qx = O.quantize_dynamic(x, "bf16", O.E4M3)
+    q1 = O.quantize_dynamic(w1, "bf16", O.E4M3)
+    q2 = O.quantize_dynamic(w2, "bf16", O.E4M3)
+    ref1 = O.mm_quantized(qx["codes"], O.E4M3, q1["codes"], O.E4M3, O.E4M3, qx["scale_inv"], q1["scale_inv"],
+                          ring=ry0)
+    got1 = np_codes(y1)
+    same = got1 == ref1["codes"][0]
+    assert same.mean() >= 0.99
+    # the device's codes feed layer 2; its output must match the oracle on those codes
+    assert f32_words(y1_sinv)[0] == as_bits(ref1["scale_inv"])
+    check(np_bf16_bits(y2), got1, O.E4M3, q2["codes"], O.E4M3, ref1["scale_inv"], q2["scale_inv"],
+          O.widen_to_f32(b2, "bf16").astype(np.float64), tag="chain layer 2")
