@@ -219,7 +219,9 @@ def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_inv
            b_scale_inv: torch.Tensor | None = None, bias: torch.Tensor | None = None,
            out: torch.Tensor | None = None) -> torch.Tensor:
     """C = bf16(A B^T * sa * sb + bias) for fp8 codes A [(batch,) M, K] and
-    B [(batch,) N, K]; a size-1 (or stride-0) batch dimension broadcasts."""
+    B [(batch,) N, K]; a size-1 (or stride-0) batch dimension broadcasts.
+    An operand that is a transposed view (unit stride along its rows, e.g.
+    codes_t.t()) is read K-major through fp8_mm_ex's layout tags."""
     return _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, None, None, out, None, ex=False)
 
 
@@ -237,6 +239,23 @@ def fp8_mm_ex(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_
                     out_scale, out_ring, out_scale_inv, out_amax)
 
 
+def _operand_ld(t3: torch.Tensor, name: str):
+    """Leading dimension of a [batch, rows, K] operand and whether it is
+    K-major (a transposed view of [K, rows] storage: unit stride along rows),
+    which the library reads through the FP8MI_A_KM / FP8MI_B_KM layout tags."""
+    rows, K = t3.shape[1], t3.shape[2]
+    if K <= 1 or t3.stride(2) == 1:
+        return (t3.stride(1) if rows > 1 else K), False
+    if rows <= 1 or t3.stride(1) == 1:
+        ld = t3.stride(2) if K > 1 else rows
+        # the library reads K full rows of ld bytes (the last row's padding included)
+        last = t3.storage_offset() + (t3.shape[0] - 1) * t3.stride(0) + K * ld
+        if last > t3.untyped_storage().nbytes():
+            raise ValueError(f"K-major operand {name} must span {K} full rows of {ld} bytes in its storage")
+        return ld, True
+    raise ValueError(f"operand {name} needs unit stride along K or along its rows")
+
+
 def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_scale, out, out_fmt,
              out_scale=None, out_ring=None, out_scale_inv=None, out_amax=None, ex=True):
     a, b = _as_codes(a), _as_codes(b)
@@ -249,13 +268,11 @@ def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_
         raise ValueError("batch sizes must match or be 1")
     M, K = a3.shape[1], a3.shape[2]
     N = b3.shape[1]
-    for t in (a3, b3):
-        if t.shape[-1] > 1 and t.stride(-1) != 1:
-            raise ValueError("operands need unit stride along K")
+    lda, a_km = _operand_ld(a3, "a")
+    ldb, b_km = _operand_ld(b3, "b")
+    layout = (1 if a_km else 0) | (2 if b_km else 0)
     sa = 0 if a3.shape[0] == 1 else a3.stride(0)
     sb = 0 if b3.shape[0] == 1 else b3.stride(0)
-    lda = a3.stride(1) if M > 1 else K
-    ldb = b3.stride(1) if N > 1 else K
     c_dt = BF16 if out_fmt is None else FP8_E4M3 + _fmt(out_fmt)
     if out is None:
         shape = (batch, M, N) if (a.dim() == 3 or b.dim() == 3) else (M, N)
@@ -271,13 +288,13 @@ def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_
         bias, bias_dt = _as_codes(bias), FP8_E4M3 + _fmt(bias_fmt)
     else:
         bias_dt = _DT[bias.dtype]
-    if not ex:
+    if not ex and layout == 0:
         _check(lib().fp8_mm(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
                             _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(out), ldc, sc,
                             _stream(a)))
         return out
     rp, h = _ring_args(out_ring)
-    _check(lib().fp8_mm_ex(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
+    _check(lib().fp8_mm_ex(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch, layout,
                            _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(bias_scale), _ptr(out),
                            c_dt, ldc, sc, _ptr(out_scale), rp, h, _ptr(out_scale_inv), _ptr(out_amax), _stream(a)))
     return out

@@ -19,7 +19,7 @@ SIGNATURES = {
     "fp8_amax_fold": (C.c_int, [_P, _I32, _P, _I, _P]),
     "fp8_mm": (C.c_int, [_P, _I, _I64, _I64, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P,
                          _I64, _I64, _P]),
-    "fp8_mm_ex": (C.c_int, [_P, _I, _I64, _I64, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P,
+    "fp8_mm_ex": (C.c_int, [_P, _I, _I64, _I64, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _I, _P,
                             _P, _I, _I64, _I64, _P, _P, _I32, _P, _P, _P]),
     "fp8_bias_grad": (C.c_int, [_P, _I, _I64, _I64, _I64, _P, _P, C.c_size_t, _P]),
     "fp8_bias_grad_workspace_bytes": (C.c_size_t, [_I64, _I64]),

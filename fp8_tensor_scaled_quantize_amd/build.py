@@ -14,7 +14,7 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["abi.hip", "quantize.hip", "mm_fp8.hip", "mm_fp8_q8.hip", "grad_bias.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "mm_fp8.hip", "mm_fp8_q8.hip", "mm_fp8_km.hip", "grad_bias.hip"]
 LIB = os.path.join(PKG, "libfp8mi.so")
 
 HIPCC_FLAGS = [

@@ -193,13 +193,14 @@ fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const float* amax, 
 }
 
 fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, const uint8_t* b, int fmt_b,
-                       int64_t ldb, int64_t stride_b, int64_t M, int64_t N, int64_t K, int64_t batch,
+                       int64_t ldb, int64_t stride_b, int64_t M, int64_t N, int64_t K, int64_t batch, int layout,
                        const float* a_scale_inv, const float* b_scale_inv, const void* bias, int bias_dtype,
                        const float* bias_scale, void* c, int c_dtype, int64_t ldc, int64_t stride_c,
                        const float* c_scale, uint32_t* c_ring, int32_t c_hist_len, float* c_scale_inv_out,
                        float* c_amax_out, void* stream) {
   if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b))
     return fail(FP8MI_ERR_ENUM, "fmt_a %d / fmt_b %d must be FP8MI_E4M3/FP8MI_E5M2", fmt_a, fmt_b);
+  if (layout < 0 || layout > 3) return fail(FP8MI_ERR_ENUM, "layout %d is not a combination of FP8MI_A_KM / FP8MI_B_KM", layout);
   const bool fp8_bias = bias_dtype == FP8MI_FP8_E4M3 || bias_dtype == FP8MI_FP8_E5M2;
   if (bias && !valid_dtype(bias_dtype) && !fp8_bias)
     return fail(FP8MI_ERR_ENUM, "bias_dtype %d is not F32/F16/BF16/FP8_E4M3/FP8_E5M2", bias_dtype);
@@ -214,6 +215,7 @@ fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_
   } else if (c_scale || c_ring || c_scale_inv_out || c_amax_out) {
     return fail(FP8MI_ERR_ARG, "output scale, ring, scale_inv and amax are for an fp8 output only");
   }
+  if (fp8_out && layout != 0) return fail(FP8MI_ERR_UNSUPPORTED, "K-major operands take a bf16 output");
   if (M < 0 || N < 0 || K < 0 || batch < 0)
     return fail(FP8MI_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld batch=%lld", (long long)M, (long long)N,
                 (long long)K, (long long)batch);
@@ -233,8 +235,10 @@ fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_
   if (!c) return fail(FP8MI_ERR_NULL, "c is NULL");
   if (K > 0 && (!a || !b)) return fail(FP8MI_ERR_NULL, "a or b is NULL");
   if (ldc < N) return fail(FP8MI_ERR_SHAPE, "ldc %lld < N %lld", (long long)ldc, (long long)N);
-  if (K > 0 && (lda < K || ldb < K))
-    return fail(FP8MI_ERR_SHAPE, "lda %lld / ldb %lld < K %lld", (long long)lda, (long long)ldb, (long long)K);
+  const int64_t row_a = (layout & 1) ? M : K, row_b = (layout & 2) ? N : K;  // bytes per stored row
+  if (K > 0 && (lda < row_a || ldb < row_b))
+    return fail(FP8MI_ERR_SHAPE, "lda %lld / ldb %lld shorter than a stored row (%lld / %lld)", (long long)lda,
+                (long long)ldb, (long long)row_a, (long long)row_b);
   if (stride_a < 0 || stride_b < 0 || stride_c < 0) return fail(FP8MI_ERR_STRIDE, "negative batch stride");
   if (batch > 1 && stride_c < M * ldc)
     return fail(FP8MI_ERR_STRIDE, "stride_c %lld < M*ldc %lld: batches would overlap", (long long)stride_c,
@@ -257,8 +261,11 @@ fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_
   p.a_scale_inv = a_scale_inv; p.b_scale_inv = b_scale_inv;
   p.bias = bias; p.bias_dtype = bias ? bias_dtype : -1; p.bias_scale = bias_scale;
   p.c = c; p.ldc = ldc; p.stride_c = stride_c;
-  if (fp8_out && !(p.a_extent_from(0) < (1ll << 31) && p.b_extent_from(0) < (1ll << 31) && K < (1ll << 30)))
-    return fail(FP8MI_ERR_UNSUPPORTED, "an fp8 output needs operand extents below 2^31 bytes");
+  p.layout = layout;
+  const int64_t ext_a = (layout & 1) ? p.a_extent_km(0) : p.a_extent_from(0);
+  const int64_t ext_b = (layout & 2) ? p.b_extent_km(0) : p.b_extent_from(0);
+  if ((fp8_out || layout != 0) && !(ext_a < (1ll << 31) && ext_b < (1ll << 31) && K < (1ll << 30)))
+    return fail(FP8MI_ERR_UNSUPPORTED, "an fp8 output or a K-major operand needs operand extents below 2^31 bytes");
   return from_hip(launch_mm(p, fmt_a, fmt_b, static_cast<hipStream_t>(stream)), "mm launch");
 }
 
@@ -267,7 +274,7 @@ fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a, 
                     const float* a_scale_inv, const float* b_scale_inv, const void* bias, int bias_dtype, void* c,
                     int64_t ldc, int64_t stride_c, void* stream) {
   if (bias && !valid_dtype(bias_dtype)) return fail(FP8MI_ERR_ENUM, "bias_dtype %d is not F32/F16/BF16", bias_dtype);
-  return fp8_mm_ex(a, fmt_a, lda, stride_a, b, fmt_b, ldb, stride_b, M, N, K, batch, a_scale_inv, b_scale_inv, bias,
+  return fp8_mm_ex(a, fmt_a, lda, stride_a, b, fmt_b, ldb, stride_b, M, N, K, batch, 0, a_scale_inv, b_scale_inv, bias,
                    bias_dtype, nullptr, c, FP8MI_BF16, ldc, stride_c, nullptr, nullptr, 0, nullptr, nullptr, stream);
 }
 

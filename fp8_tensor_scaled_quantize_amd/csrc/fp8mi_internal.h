@@ -52,15 +52,24 @@ struct MmArgs {
   int c_H = 0;
   float* c_scale_inv_out = nullptr;
   float* c_amax_out = nullptr;
+  int layout = 0;                     // bit 0: A is [K, M] (K-major), bit 1: B is [K, N]
 
   // Bytes of one batch's A (B) from row r on: the last row ends at K.
   __host__ __device__ int64_t a_extent_from(int64_t r) const { return r < M ? (M - 1 - r) * lda + K : 0; }
   __host__ __device__ int64_t b_extent_from(int64_t r) const { return r < N ? (N - 1 - r) * ldb + K : 0; }
+  // K-major operands ([K, ld] arrays of K full rows): bytes from column r of
+  // row 0 to the end of row K - 1 including its padding, so the extent ends
+  // on a 16-byte chunk boundary (lda % 16 == 0, r % 16 == 0): the raw-buffer
+  // range check zeroes a straddling 16-byte access as a whole.
+  __host__ __device__ int64_t a_extent_km(int64_t r) const { return (r < M && K > 0) ? K * lda - r : 0; }
+  __host__ __device__ int64_t b_extent_km(int64_t r) const { return (r < N && K > 0) ? K * ldb - r : 0; }
 };
 
 hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 // fp8-output GEMM (p.out_fmt >= 0, operand extents below 2^31 bytes).
 hipError_t launch_mm_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+// bf16-output GEMM with K-major operand(s) (p.layout != 0, extents below 2^31 bytes).
+hipError_t launch_mm_km(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 // One fp32 word set to 0 on the stream (a fill kernel, capturable).
 hipError_t launch_zero_word(float* p, hipStream_t st);
 

@@ -25,6 +25,42 @@ constexpr int kMmThreads = 256;
 // position the group within it).
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 1) | (row & 4); }
 
+// K-major operand tiles (an operand given as [K, rows], the tile's rows
+// contiguous): LDS holds 128 k-rows of W bytes (CPR = W / 16 chunks each);
+// the 16-byte chunk c of k-row kr sits at chunk position
+// (c + rot(kr)) mod CPR, rot(kr) = (kr & 7) + 8 * bit 5 of kr -- a
+// permutation for any CPR (192-byte rows included).  A fragment read (below)
+// touches 8 consecutive k-rows per 16-lane group at one chunk: the rotation
+// puts them on 8 distinct 4-bank groups for W = 128, 192 and 256, and bit 5
+// (which separates the lane groups 0/2 from 1/3) moves the other half-wave
+// onto the remaining banks.
+template <int CPR> __device__ __forceinline__ int km_pos(int c, int kr) {
+  return (c + (kr & 7) + (((kr >> 5) & 1) << 3)) % CPR;
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i* lds_v2i_ptr;
+
+// MFMA operand fragment (lane l: tile row rb + l%16, k = 32(l/16) .. +31)
+// from a K-major tile with ds_read_b64_tr_b8.  Measured lane layout of that
+// instruction: within each group of 16 lanes, output lane 8h + c receives in
+// byte j the byte c of the 8 bytes addressed by lane 2j + h.  So lane a = 2j + h
+// of a group addresses k-row kb + j at column rb + 8h, and every lane receives
+// its own row's 8 consecutive k; four reads cover k = 32g .. 32g + 31.
+template <int W> __device__ __forceinline__ v8i lds_frag_km(const uint8_t* S, int rb, int lane) {
+  const int g = lane >> 4, a = lane & 15, j = a >> 1, h = a & 1;
+  v8i r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int kr = 32 * g + 8 * q + j;
+    const int pos = km_pos<W / 16>(rb >> 4, kr);
+    const v2i d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(S + kr * W + pos * 16 + 8 * h));
+    r[2 * q] = d[0];
+    r[2 * q + 1] = d[1];
+  }
+  return r;
+}
+
 __device__ __forceinline__ v8i lds_frag(const uint8_t* S, int row, int g) {
   const int sw = swz(row);
   const uint4 lo = *reinterpret_cast<const uint4*>(S + row * kBK + (((2 * g) ^ sw) << 4));
@@ -157,9 +193,12 @@ __device__ __forceinline__ void tile_coords(int64_t wg, int64_t tiles_m, int64_t
   tn = r / rows_here;
 }
 
-template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS, int OUT>
+// LAY: bit 0 -- A given K-major ([K, M], lda >= M), bit 1 -- B given K-major
+// ([K, N], ldb >= N); otherwise the operand is [rows, K] (NT).
+template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS, int OUT, int LAY>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma(MmArgs p, int64_t tiles_m,
                                                                                  int64_t tiles_n, int group_m) {
+  constexpr bool KMA = (LAY & 1) != 0, KMB = (LAY & 2) != 0;
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TI = WM / 16, TJ = WN / 16;
@@ -179,9 +218,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
   int64_t tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int ext_a = (int)p.a_extent_from(m0), ext_b = (int)p.b_extent_from(n0);
-  const v4i rsa = buffer_rsrc(p.a + bz * p.stride_a + m0 * p.lda, ext_a);
-  const v4i rsb = buffer_rsrc(p.b + bz * p.stride_b + n0 * p.ldb, ext_b);
+  const int ext_a = (int)(KMA ? p.a_extent_km(m0) : p.a_extent_from(m0));
+  const int ext_b = (int)(KMB ? p.b_extent_km(n0) : p.b_extent_from(n0));
+  const v4i rsa = buffer_rsrc(p.a + bz * p.stride_a + (KMA ? m0 : m0 * p.lda), ext_a);
+  const v4i rsb = buffer_rsrc(p.b + bz * p.stride_b + (KMB ? n0 : n0 * p.ldb), ext_b);
   // Lane l of a 1 KiB load fills LDS row r0 + l/8 (r0 a multiple of 8) at
   // chunk position l%8, so it fetches logical chunk (l%8) ^ swz(l/8).
   const int lr = lane >> 3, lc = (lane & 7) ^ swz(lr);
@@ -189,6 +229,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
   const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
   const uint32_t va = lr * lda + 16 * lc, vb = lr * ldb + 16 * lc;
   const int K = (int)p.K;
+  // K-major operands: load instruction ii fills LDS chunks 64 ii .. 64 ii + 63
+  // of the stage; lane l's chunk q = 64 ii + l is position q % CPR of k-row
+  // q / CPR, so it fetches the chunk c whose km_pos is that position.  The
+  // step's k0 enters as the scalar offset k0 * ld.
+  constexpr int CPR_A = BM / 16, CPR_B = BN / 16;
+
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
 
   // Issue one stage of loads (this wave's 4 + 4 instructions).
@@ -203,12 +249,30 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 #pragma unroll
     for (int q = 0; q < (LA > LB ? LA : LB); ++q) {
       if (q < LA) {
-        const int r0 = (wid * LA + q) * 8;
-        dma16(rsa, as + r0 * kBK, past ? ext_a : (int)(va + (uint32_t)r0 * lda), k0);
+        if constexpr (KMA) {
+          const int qq = (wid * LA + q) * 64 + lane;
+          const int kr = qq / CPR_A, pos = qq % CPR_A;  // k-row within the step; rows past K read zero
+          const int rot = ((kr & 7) + (((kr >> 5) & 1) << 3)) % CPR_A;
+          const uint32_t c = (uint32_t)((pos + CPR_A - rot) % CPR_A);  // inverse of km_pos
+          dma16(rsa, as + (wid * LA + q) * 1024, k0 + kr >= K ? ext_a : (int)((uint32_t)kr * lda + 16 * c),
+                (int)((uint32_t)k0 * lda));
+        } else {
+          const int r0 = (wid * LA + q) * 8;
+          dma16(rsa, as + r0 * kBK, past ? ext_a : (int)(va + (uint32_t)r0 * lda), k0);
+        }
       }
       if (q < LB) {
-        const int r0 = (wid * LB + q) * 8;
-        dma16(rsb, bs + r0 * kBK, past ? ext_b : (int)(vb + (uint32_t)r0 * ldb), k0);
+        if constexpr (KMB) {
+          const int qq = (wid * LB + q) * 64 + lane;
+          const int kr = qq / CPR_B, pos = qq % CPR_B;
+          const int rot = ((kr & 7) + (((kr >> 5) & 1) << 3)) % CPR_B;
+          const uint32_t c = (uint32_t)((pos + CPR_B - rot) % CPR_B);  // inverse of km_pos
+          dma16(rsb, bs + (wid * LB + q) * 1024, k0 + kr >= K ? ext_b : (int)((uint32_t)kr * ldb + 16 * c),
+                (int)((uint32_t)k0 * ldb));
+        } else {
+          const int r0 = (wid * LB + q) * 8;
+          dma16(rsb, bs + r0 * kBK, past ? ext_b : (int)(vb + (uint32_t)r0 * ldb), k0);
+        }
       }
     }
   };
@@ -230,10 +294,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
     if (kt + 1 < nk) issue_all((kt + 1) & 1, (kt + 1) * kBK);
     v8i bfr[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) bfr[j] = lds_frag(Bs, wn * WN + 16 * j + r16, g);
+    for (int j = 0; j < TJ; ++j)
+      bfr[j] = KMB ? lds_frag_km<BN>(Bs, wn * WN + 16 * j, lane) : lds_frag(Bs, wn * WN + 16 * j + r16, g);
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      const v8i af = lds_frag(As, wm * WM + 16 * i + r16, g);
+      const v8i af = KMA ? lds_frag_km<BM>(As, wm * WM + 16 * i, lane) : lds_frag(As, wm * WM + 16 * i + r16, g);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_nt<FA, FB>(bfr[j], af, acc[i][j]);
     }
@@ -387,11 +452,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 // 128x128 is reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128
 // kernel remains for operands whose byte extent does not fit a 32-bit buffer
 // offset.
-template <int FA, int FB, int BM, int BN, int WM_, int WN_, int MINB, int OUT>
+template <int FA, int FB, int BM, int BN, int WM_, int WN_, int MINB, int OUT, int LAY = 0>
 static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
   const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
-  hipLaunchKernelGGL((mm_fp8_dma<FA, FB, BM, BN, WM_, WN_, MINB, OUT>), grid, dim3(64 * WM_ * WN_), 0, st, p,
+  hipLaunchKernelGGL((mm_fp8_dma<FA, FB, BM, BN, WM_, WN_, MINB, OUT, LAY>), grid, dim3(64 * WM_ * WN_), 0, st, p,
                      tiles_m, tiles_n, 4);
   return hipGetLastError();
 }
@@ -421,7 +486,9 @@ template <int FA, int FB, int OUT> static hipError_t launch_dma_family(const MmA
 
 // Operand extents the 32-bit buffer offsets of the big-tile kernels cover.
 static inline bool mm_fits31(const MmArgs& p) {
-  return p.a_extent_from(0) < (1ll << 31) && p.b_extent_from(0) < (1ll << 31) && p.K < (1ll << 30);
+  const int64_t ea = (p.layout & 1) ? p.a_extent_km(0) : p.a_extent_from(0);
+  const int64_t eb = (p.layout & 2) ? p.b_extent_km(0) : p.b_extent_from(0);
+  return ea < (1ll << 31) && eb < (1ll << 31) && p.K < (1ll << 30);
 }
 
 }  // namespace fp8mi

@@ -216,15 +216,27 @@ FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t 
  *              one fold of it into the ring, c_scale_inv_out = 1 / s_c and
  *              c_amax_out = amax (both optional).  Operand extents must stay
  *              below 2^31 bytes (else FP8MI_ERR_UNSUPPORTED).
+ *   layout     0, or FP8MI_A_KM and / or FP8MI_B_KM: an operand given K-major
+ *              (e.g. a transposed view of a row-major [K, M] array), read
+ *              without a transposed copy (the pages' layout tags from .t()
+ *              views: log:tests/extension, the commit taking transposed and
+ *              3-D operands into the GEMM).  A K-major A is a [K, lda] array
+ *              of K full rows (K * lda readable bytes per batch, the last
+ *              row's padding included) with lda >= M (B: [K, ldb], ldb >= N),
+ *              lda % 16 == 0, extents below 2^31 bytes and a bf16 output
+ *              (else FP8MI_ERR_UNSUPPORTED); the result is that of the same
+ *              operands in NT form, bit for bit.
  * Other arguments and requirements as fp8_mm.  M, N or batch 0 writes no
  * codes; an fp8 output then still folds amax 0 into its ring (or writes
  * 1 / s_c and amax 0).  y is fp32, so its accumulation error is that of
  * fp8_mm before the bf16 rounding; an output near a code boundary may take
  * the neighbouring code.
  */
+#define FP8MI_A_KM 1 /* layout tag: A stored K-major, A(b,i,k) = a[b * stride_a + k * lda + i] */
+#define FP8MI_B_KM 2 /* layout tag: B stored K-major, B(b,j,k) = b[b * stride_b + k * ldb + j] */
 FP8MI_API fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a,
                                  const uint8_t* b, int fmt_b, int64_t ldb, int64_t stride_b,
-                                 int64_t M, int64_t N, int64_t K, int64_t batch,
+                                 int64_t M, int64_t N, int64_t K, int64_t batch, int layout,
                                  const float* a_scale_inv, const float* b_scale_inv,
                                  const void* bias, int bias_dtype, const float* bias_scale,
                                  void* c, int c_dtype, int64_t ldc, int64_t stride_c,

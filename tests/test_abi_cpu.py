@@ -205,10 +205,10 @@ def test_quantize_dynamic_rejects(L):
 def test_mm_ex_rejects(L):
     f = L.fp8_mm_ex
 
-    def call(a=FAKE, fa=0, lda=32, sa=0, b=FAKE, fb=0, ldb=32, sb=0, M=4, N=4, K=32, batch=1, bias=None, bdt=0,
-             bsc=None, c=FAKE, cdt=2, ldc=4, sc=16, cscale=None, cring=None, h=0, sinv=None, amax=None):
-        return f(a, fa, lda, sa, b, fb, ldb, sb, M, N, K, batch, None, None, bias, bdt, bsc, c, cdt, ldc, sc, cscale,
-                 cring, h, sinv, amax, None)
+    def call(a=FAKE, fa=0, lda=32, sa=0, b=FAKE, fb=0, ldb=32, sb=0, M=4, N=4, K=32, batch=1, lay=0, bias=None,
+             bdt=0, bsc=None, c=FAKE, cdt=2, ldc=4, sc=16, cscale=None, cring=None, h=0, sinv=None, amax=None):
+        return f(a, fa, lda, sa, b, fb, ldb, sb, M, N, K, batch, lay, None, None, bias, bdt, bsc, c, cdt, ldc, sc,
+                 cscale, cring, h, sinv, amax, None)
 
     assert call(fa=2) == ENUM
     assert call(cdt=0) == ENUM                        # fp32 output is not offered
@@ -227,5 +227,12 @@ def test_mm_ex_rejects(L):
     assert call(cdt=3, cscale=FAKE, c=None) == NULL
     assert call(cdt=3, cscale=FAKE, ldc=3) == SHAPE
     assert call(cdt=3, cscale=FAKE, K=24, lda=24, ldb=24) == UNSUP
+    # layout tags
+    assert call(lay=4) == ENUM
+    assert call(lay=-1) == ENUM
+    assert call(lay=1, cdt=3, cscale=FAKE) == UNSUP   # K-major operands take a bf16 output
+    assert call(lay=1, M=64, lda=48) == SHAPE         # K-major A: lda must cover M
+    assert call(lay=2, N=64, ldb=48) == SHAPE
+    assert call(lay=1, M=64, lda=72) == UNSUP         # lda % 16
     # the plain fp8_mm refuses an fp8 bias type (it has no bias scale)
     assert L.fp8_mm(FAKE, 0, 32, 0, FAKE, 0, 32, 0, 4, 4, 32, 1, None, None, FAKE, 3, FAKE, 4, 16, None) == ENUM
