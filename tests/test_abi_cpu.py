@@ -236,3 +236,25 @@ def test_mm_ex_rejects(L):
     assert call(lay=1, M=64, lda=72) == UNSUP         # lda % 16
     # the plain fp8_mm refuses an fp8 bias type (it has no bias scale)
     assert L.fp8_mm(FAKE, 0, 32, 0, FAKE, 0, 32, 0, 4, 4, 32, 1, None, None, FAKE, 3, FAKE, 4, 16, None) == ENUM
+
+
+def test_binding_maps_transposed_views_to_layout_tags():
+    """The binding reads an operand that is a transposed view (unit stride
+    along its rows) K-major, with the storage's row length as leading
+    dimension, and refuses a K-major view whose storage lacks the K full rows
+    the library reads; host-side logic only (CPU tensors, no library call)."""
+    import torch
+    from fp8_tensor_scaled_quantize_amd import _operand_ld
+    a = torch.zeros((64, 96), dtype=torch.uint8)                      # [M, K] row-major
+    assert _operand_ld(a.unsqueeze(0), "a") == (96, False)
+    at = torch.zeros((96, 80), dtype=torch.uint8)                     # [K, M + pad] storage
+    v = at[:, :64].t()                                                 # [M, K] view, unit stride along M
+    assert _operand_ld(v.unsqueeze(0), "a") == (80, True)
+    b3 = torch.zeros((3, 96, 48), dtype=torch.uint8).transpose(1, 2)  # batched K-major view
+    assert _operand_ld(b3, "b") == (48, True)
+    with pytest.raises(ValueError):
+        _operand_ld(torch.zeros((64, 96), dtype=torch.uint8)[:, ::2].unsqueeze(0), "a")  # no unit stride
+    flat = torch.zeros(96 * 80 - 8, dtype=torch.uint8)                # last row short of its padding
+    short = torch.as_strided(flat, (64, 96), (1, 80))
+    with pytest.raises(ValueError):
+        _operand_ld(short.unsqueeze(0), "a")
