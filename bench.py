@@ -223,8 +223,11 @@ def main():
     total_ms = timed(lambda i: step(args.warmup + i), args.steps) * args.steps
     nlaunch = max(10, args.steps)
     names = ["quantize_row", "quantize_transposed", "quantize_dual", "mm_fp8", "quantize_dynamic_row",
-             "quantize_dynamic_dual", "mm_fp8_out_e4m3"]
+             "quantize_dynamic_dual", "mm_fp8_out_e4m3", "mm_fp8_kmajor"]
     C8_out = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    # K-major copies of the GEMM operands: [K, M] / [K, N] storage read through transposed views
+    A_km = [a.t().contiguous() for a in A]
+    B_km = [b.t().contiguous() for b in B]
     ring_c = fp8mi.new_ring(HIST, 1.0, dev)
     ws_dyn = torch.empty(fp8mi.DYNAMIC_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     launches = {
@@ -244,6 +247,9 @@ def main():
         # FP8-out GEMM: the quantizing epilogue with the output's ring fold
         "mm_fp8_out_e4m3": lambda i: fp8mi.fp8_mm_ex(A[i % nm], B[i % nm], fp8mi.E4M3, fp8mi.E4M3, sa, sb, bias,
                                                      out=C8_out, out_fmt=fp8mi.E4M3, out_ring=ring_c),
+        # layout tags: both operands K-major (transposed views), bf16 out
+        "mm_fp8_kmajor": lambda i: fp8mi.fp8_mm(A_km[i % nm].t(), B_km[i % nm].t(), fp8mi.E4M3, fp8mi.E4M3, sa, sb,
+                                                bias, out=C_out),
     }
     us = [timed(launches[nme], nlaunch) * 1e3 for nme in names]
     qbytes = {"quantize_row": R * C * 3, "quantize_transposed": R * C * 3, "quantize_dual": R * C * 4,
@@ -295,12 +301,16 @@ def main():
         "mm_fp8_out_e4m3": {"us_per_launch": round(float(us[names.index("mm_fp8_out_e4m3")]), 3),
                             "TFLOPs": round(flops / (us[names.index("mm_fp8_out_e4m3")] * 1e-6) / 1e12, 1),
                             "workload": "4096^3 E4M3 + fp32 bias -> E4M3 codes, ring scale + amax fold (H=16)"},
+        "mm_fp8_kmajor": {"us_per_launch": round(float(us[names.index("mm_fp8_kmajor")]), 3),
+                          "TFLOPs": round(flops / (us[names.index("mm_fp8_kmajor")] * 1e-6) / 1e12, 1),
+                          "workload": "4096^3 E4M3 + fp32 bias -> bf16, A and B given K-major (layout tags)"},
     }
     traffic = counter_traffic()
     if traffic:
-        t = traffic.get("mm_fp8_out_e4m3")
-        if t:
-            out["mm_fp8_out_e4m3"]["traffic"] = int(t["fetch"] + t["write"])
+        for name in ("mm_fp8_out_e4m3", "mm_fp8_kmajor"):
+            t = traffic.get(name)
+            if t:
+                out[name]["traffic"] = int(t["fetch"] + t["write"])
         for key, name in (("roofline", "mm_fp8"), ("roofline_quantize", "quantize_dual")):
             t = traffic.get(name)
             if t:
