@@ -1,6 +1,8 @@
 /*
- * fp8mi -- FP8 per-tensor scaled quantize, delayed-scaling amax history fold
- * and per-tensor-scaled fp8 GEMM for AMD Instinct MI355X (gfx950).
+ * fp8mi -- FP8 per-tensor scaled quantize (delayed scaling with an in-kernel
+ * amax history fold, or current scaling), per-tensor-scaled fp8 GEMM (fused
+ * bias, bf16 or quantized fp8 output, layout tags) and the bias gradient, for
+ * AMD Instinct MI355X (gfx950).
  *
  * C ABI.  Every pointer argument named "device" is a device (HBM) pointer;
  * every call is asynchronous on `stream` (a hipStream_t passed as void*;
