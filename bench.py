@@ -147,6 +147,91 @@ def time_training_step(torch, fp8mi, synth, steps, warmup):
             "launches_per_step": 9}
 
 
+def sweep(torch, fp8mi, synth, dev, prime):
+    """Throughput of every other config's GEMM and quantize shapes (back-to-back
+    launches over two input sets, one untimed call first), with the pages'
+    NVIDIA L20 figure where they give one (context, other hardware)."""
+    def timed_us(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        prime()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    def codes(shape, seed):
+        x = synth.device_gaussian(shape, 1.0, torch.bfloat16, seed, dev)
+        ring = fp8mi.new_ring(1, 1.0, dev)
+        fp8mi.fp8_quantize(x.reshape(-1, shape[-1]), fp8mi.E4M3, ring=ring)
+        return fp8mi.fp8_quantize(x.reshape(-1, shape[-1]), fp8mi.E4M3, ring=ring).reshape(shape)
+
+    out = {}
+    sa = torch.tensor([0.5], dtype=torch.float32, device=dev)
+    sb = torch.tensor([0.25], dtype=torch.float32, device=dev)
+    gemms = [  # name, batch, M, N, K, broadcast B, bias, L20 TF/s
+        ("square 1024^3", 1, 1024, 1024, 1024, False, False, 106.3),
+        ("square 2048^3", 1, 2048, 2048, 2048, False, False, 178.2),
+        ("square 8192^3", 1, 8192, 8192, 8192, False, False, 200.0),
+        ("skinny 64x8192x2048", 1, 64, 8192, 2048, False, False, 94.0),
+        ("skinny 1024x1536x2048", 1, 1024, 1536, 2048, False, False, 108.0),
+        ("odd N 1024x1537x2048 + bias", 1, 1024, 1537, 2048, False, True, None),
+        ("bmm 64 x 512^3", 64, 512, 512, 512, False, False, 161.0),
+        ("bmm 8 x 1024x2048x2048", 8, 1024, 2048, 2048, False, False, 186.0),
+        ("bmm 8 x 1024x2048x2048, B stride 0", 8, 1024, 2048, 2048, True, False, None),
+        ("linear 2048x1536x1536 + bias", 1, 2048, 1536, 1536, False, True, None),
+        ("linear 2048x6912x1536 + bias", 1, 2048, 6912, 1536, False, True, None),
+        ("linear 2048x1536x6912 + bias", 1, 2048, 1536, 6912, False, True, None),
+    ]
+    for gi, (name, batch, M, N, K, bcast, has_bias, l20) in enumerate(gemms):
+        sets = []
+        for r in range(2):
+            a = codes((batch, M, K) if batch > 1 else (M, K), 7000 + 10 * gi + r)
+            b = codes((N, K), 7100 + 10 * gi + r)
+            if batch > 1:
+                b = b.unsqueeze(0).expand(batch, N, K) if bcast else codes((batch, N, K), 7200 + 10 * gi + r)
+            sets.append((a, b))
+        bias = synth.device_gaussian((N,), 1.0, torch.float32, 7300 + gi, dev) if has_bias else None
+        cbuf = torch.empty((batch, M, N) if batch > 1 else (M, N), dtype=torch.bfloat16, device=dev)
+        flops = 2.0 * batch * M * N * K
+        n = max(5, min(200, int(2e-3 / (flops / 2.0e15))))
+        us = timed_us(lambda i: fp8mi.fp8_mm(sets[i % 2][0], sets[i % 2][1], fp8mi.E4M3, fp8mi.E4M3, sa, sb, bias,
+                                             out=cbuf), n)
+        tf = flops / (us * 1e-6) / 1e12
+        out[name] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "L20_TFLOPs": l20}
+        del sets, cbuf
+    quants = [  # name, rows, cols, layout, misaligned base, L20 GB/s
+        ("transposed 2048x1536", 2048, 1536, "t", False, 294.0),
+        ("dual 2048x1536", 2048, 1536, "dual", False, 329.0),
+        ("row 8192x1535 (odd width)", 8192, 1535, "row", False, None),
+        ("dual 8192x1536, base + 1 element", 8192, 1536, "dual", True, 384.0),
+    ]
+    ring = fp8mi.new_ring(16, 1.0, dev)
+    for qi, (name, R, C, lay, mis, l20) in enumerate(quants):
+        nset = 12 if R * C * 2 * 12 > 300e6 else 4
+        bufs = [synth.device_gaussian((R * C + 8,), 1.0, torch.bfloat16, 7400 + 10 * qi + r, dev) for r in range(nset)]
+        xs = [b[1:1 + R * C].view(R, C) if mis else b[:R * C].view(R, C) for b in bufs]
+        o_r = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        o_t = torch.empty((C, R), dtype=torch.uint8, device=dev)
+        if lay == "row":
+            fn = lambda i: fp8mi.fp8_quantize(xs[i % nset], fp8mi.E4M3, False, out=o_r, ring=ring)
+        elif lay == "t":
+            fn = lambda i: fp8mi.fp8_quantize(xs[i % nset], fp8mi.E4M3, True, out=o_t, ring=ring)
+        else:
+            fn = lambda i: fp8mi.fp8_quantize_dual(xs[i % nset], fp8mi.E4M3, out_row=o_r, out_t=o_t, ring=ring)
+        us = timed_us(fn, 50)
+        by = R * C * (4 if lay == "dual" else 3)
+        gbs = by / (us * 1e-6) / 1e9
+        out["quantize " + name] = {"us": round(us, 2), "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                                   "L20_GBps": l20}
+        del bufs, xs
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -318,6 +403,9 @@ def main():
                 out[key]["traffic_fetch"] = int(t["fetch"])
                 out[key]["traffic_write"] = int(t["write"])
     out["training_step"] = time_training_step(torch, fp8mi, synth, max(3, args.steps // 5), 2)
+    del A_km, B_km, xq
+    A[3:], B[3:] = [], []  # prime() keeps using the first three pairs
+    out["sweep"] = sweep(torch, fp8mi, synth, dev, prime)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

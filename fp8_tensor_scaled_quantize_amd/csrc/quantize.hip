@@ -16,7 +16,8 @@
 //    one contiguous segment of codes per store instruction.  Persistent
 //    workgroups, the next group of steps loading while one is encoded.
 //  * quantize_tiled: 128-row x 64-column tiles, 256 threads.  Each thread
-//    loads a 4-row x 8-column micro block (16-byte loads where aligned), so
+//    loads a 4-row x 8-column micro block (16-byte loads, realigned in
+//    registers when a row segment does not start on 16 bytes), so
 //    the row-layout codes leave straight from registers and the transposed
 //    codes need only a 4x4 byte transpose in registers plus one 8 KiB LDS
 //    pass, after which every lane stores 16 contiguous bytes of a transposed
@@ -148,6 +149,39 @@ template <int N> __device__ __forceinline__ float nan_free_absmax(const float* f
 // current scaling), else the ring's current scale (delayed scaling) or the
 // caller's.  DYN is a template parameter so that the delayed-scaling kernels
 // carry none of the partials code (it would cost them registers).
+// 16 * NLD bytes from src (element-aligned, any 16-byte misalignment) as NLD
+// uint4.  Global vector loads on CDNA need only dword alignment, so the data
+// comes from dword-aligned 16-byte loads at src rounded down to 4 bytes (plus
+// one more dword when that drops 2 bytes, as a 16-bit element start can),
+// shifted by v_alignbyte.  Every load holds at least one requested byte and
+// none lies beyond the last one plus 3, so all stay on pages the tensor
+// occupies.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+template <int NLD> __device__ __forceinline__ void load16_any(const char* src, uint4 (&out)[NLD]) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
+  if ((a & 15u) == 0) {
+#pragma unroll
+    for (int c = 0; c < NLD; ++c) out[c] = reinterpret_cast<const uint4*>(src)[c];
+    return;
+  }
+  const uint32_t sb = (uint32_t)(a & 3u);  // 0 or 2 (elements are 2 or 4 bytes)
+  const char* a4 = src - sb;
+  uint32_t w[4 * NLD + 1];
+#pragma unroll
+  for (int c = 0; c < NLD; ++c) {
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(a4 + 16 * c);
+    w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+  }
+  w[4 * NLD] = sb ? *reinterpret_cast<const uint32_t*>(a4 + 16 * NLD) : 0u;
+#pragma unroll
+  for (int c = 0; c < NLD; ++c) {
+    out[c].x = __builtin_amdgcn_alignbyte(w[4 * c + 1], w[4 * c], sb);
+    out[c].y = __builtin_amdgcn_alignbyte(w[4 * c + 2], w[4 * c + 1], sb);
+    out[c].z = __builtin_amdgcn_alignbyte(w[4 * c + 3], w[4 * c + 2], sb);
+    out[c].w = __builtin_amdgcn_alignbyte(w[4 * c + 4], w[4 * c + 3], sb);
+  }
+}
+
 template <int FMT, bool DYN> __device__ __forceinline__ float read_scale(const QuantArgs& p) {
   if constexpr (DYN) return scale_from_max<FMT>(parts_max(p.parts, p.nparts));
   else return p.ring ? __uint_as_float(p.ring[p.H]) : *p.scale;
@@ -327,12 +361,13 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
     for (int i = 0; i < 4; ++i) {
       const int64_t r = r0 + 4 * rg + i;
       const char* src = xb + (r * p.ld_x + cc) * EB;
-      const bool full = r < p.rows && cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+      const bool full = r < p.rows && cc + 8 <= p.cols;  // vector loads, realigned if the row start is not
       all_full &= full;
       if (full) {
         if constexpr (DT == kF32) {
-          const uint4 a = reinterpret_cast<const uint4*>(src)[0];
-          const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+          uint4 ab[2];
+          load16_any<2>(src, ab);
+          const uint4 a = ab[0], b = ab[1];
           am.add(a);
           am.add(b);
           f[i][0] = __uint_as_float(a.x); f[i][1] = __uint_as_float(a.y);
@@ -340,7 +375,9 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
           f[i][4] = __uint_as_float(b.x); f[i][5] = __uint_as_float(b.y);
           f[i][6] = __uint_as_float(b.z); f[i][7] = __uint_as_float(b.w);
         } else {
-          const uint4 a = *reinterpret_cast<const uint4*>(src);
+          uint4 a1[1];
+          load16_any<1>(src, a1);
+          const uint4 a = a1[0];
           am.add(a);
           widen2<DT>(a.x, f[i][0], f[i][1]); widen2<DT>(a.y, f[i][2], f[i][3]);
           widen2<DT>(a.z, f[i][4], f[i][5]); widen2<DT>(a.w, f[i][6], f[i][7]);
@@ -461,9 +498,9 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
 }
 
 // Persistent form (quantize_tiled_pf).  One tile's raw input for this thread: rows 4rg..4rg+3 at columns
-// 8cg..8cg+7, as 16-byte loads (two per row for f32) where the row lies
-// inside the tensor with a 16-byte aligned start; other rows are read
-// element by element while the tile is processed.
+// 8cg..8cg+7, as 16-byte loads (two per row for f32; realigned when the row
+// segment does not start on 16 bytes) where the 8 columns lie inside the
+// tensor; other rows are read element by element while the tile is processed.
 template <int DT> struct TileRaw {
   static constexpr int kLoads = In<DT>::kBytes == 4 ? 2 : 1;
   uint4 v[4][kLoads];
@@ -492,12 +529,9 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
     for (int i = 0; i < 4; ++i) {
       const int64_t r = r0 + 4 * rg + i;
       const char* src = xb + (r * p.ld_x + cc) * EB;
-      const bool full = r < p.rows && cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+      const bool full = r < p.rows && cc + 8 <= p.cols;
       L.full |= (uint32_t)full << i;
-      if (full) {
-#pragma unroll
-        for (int q = 0; q < NLD; ++q) L.v[i][q] = reinterpret_cast<const uint4*>(src)[q];
-      }
+      if (full) load16_any<NLD>(src, L.v[i]);
     }
   };
 
