@@ -198,6 +198,11 @@ constexpr int kFoldSlotStride = 32;  // words: 128 bytes between slots
 static_assert(kFoldSlots * kFoldSlotStride == 1024, "ring scratch is FP8MI_RING_SCRATCH_WORDS words");
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N> __device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ uint32_t dev_load(uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -208,7 +208,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
   static_assert(LA >= 1 && LB >= 1 && LA * 8 * NWAVES == BM && LB * 8 * NWAVES == BN, "tile / wave mismatch");
   static_assert(TI >= 1 && TJ >= 1, "wave tile below one MFMA tile");
   constexpr int CROW = BN + 8;                // bf16 per LDS row of the staged C tile (16 B pad)
-  constexpr int SMEM = 2 * STAGE > BM * CROW * 2 ? 2 * STAGE : BM * CROW * 2;
+  // LDS stages: two for the big tiles (2 x 64 KiB at 256 x 256); the small
+  // 64 x 128 tile (24 KiB per stage, two workgroups per CU) keeps three, so
+  // two K steps of loads are in flight -- small and skinny problems, which
+  // leave CUs idle and are bound by load latency, gain most from it
+  constexpr int STAGES = BM * BN <= 64 * 128 ? 3 : 2;
+  constexpr int LPW = LA + LB;  // load instructions per wave and K step
+  constexpr int SMEM = STAGES * STAGE > BM * CROW * 2 ? STAGES * STAGE : BM * CROW * 2;
   __shared__ __align__(16) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -285,13 +291,23 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 
   const int nk = (K + kBK - 1) / kBK;
   const int r16 = lane & 15, g = lane >> 4;
-  if (nk > 0) issue_all(0, 0);
-  wait_vmem();
+  // prologue: steps 0 .. STAGES-2 in flight; wait for step 0 only
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue_all(s, s * kBK);
+  if constexpr (STAGES == 3) {
+    if (nk > 1) wait_vmem_n<LPW>();
+    else wait_vmem();
+  } else {
+    wait_vmem();
+  }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* As = smem + (kt & 1) * STAGE;
+    const uint8_t* As = smem + (kt % STAGES) * STAGE;
     const uint8_t* Bs = As + BM * kBK;
-    if (kt + 1 < nk) issue_all((kt + 1) & 1, (kt + 1) * kBK);
+    // the stage refilled here was last read in step kt - 1 (all waves passed
+    // the barrier that ended it)
+    if (kt + STAGES - 1 < nk) issue_all((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * kBK);
     v8i bfr[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
@@ -302,7 +318,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 #pragma unroll
       for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_nt<FA, FB>(bfr[j], af, acc[i][j]);
     }
-    wait_vmem();
+    // step kt + 1 must have landed; step kt + 2's loads may stay in flight
+    if constexpr (STAGES == 3) {
+      if (kt + 2 < nk) wait_vmem_n<LPW>();
+      else wait_vmem();
+    } else {
+      wait_vmem();
+    }
     __syncthreads();
   }
 
