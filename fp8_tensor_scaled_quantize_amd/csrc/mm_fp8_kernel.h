@@ -470,7 +470,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 // even with part of the chip idle -- choosing 256 x 192 over 256 x 256 when it
 // needs less work per CU (rounds of workgroups x tile width: the backward
 // GEMMs of the 1536-wide linear get 256 and 216 workgroups instead of 192 and
-// 162, 10-11% faster), and the 64x128 / 4-wave kernel (two per CU) below 60%.
+// 162, 10-11% faster), and the 64x128 / 4-wave kernel (two per CU, three LDS
+// stages) below 60% -- or 64x64 when the 64x128 tiles number at most one per CU.
 // 128x128 is reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128
 // kernel remains for operands whose byte extent does not fit a 32-bit buffer
 // offset.
@@ -485,10 +486,16 @@ static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
 
 static inline int pick_tile(const MmArgs& p, int ncu) {
   static const int forced = [] { const char* e = getenv("FP8MI_MM_TILE"); return e ? atoi(e) : -1; }();
-  if (forced >= 0 && forced < 4) return forced;
+  if (forced >= 0 && forced < 6 && forced != 4) return forced;
   const int64_t tm = (p.M + 255) / 256;
   const int64_t t256 = tm * ((p.N + 255) / 256) * p.batch, t192 = tm * ((p.N + 191) / 192) * p.batch;
-  if (10 * (t256 > t192 ? t256 : t192) < 6 * (int64_t)ncu) return 2;
+  if (10 * (t256 > t192 ? t256 : t192) < 6 * (int64_t)ncu) {
+    // small problems: 64 x 128 tiles, or 64 x 64 when even those would not
+    // give every CU one (skinny shapes; measured 3-10% faster there, slower
+    // once the 64 x 128 tiles fill the chip)
+    const int64_t t128 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
+    return t128 <= (int64_t)ncu ? 5 : 2;
+  }
   // per-CU work of the big-tile family: rounds of workgroups x tile width
   const int64_t cost256 = ((t256 + ncu - 1) / ncu) * 256, cost192 = ((t192 + ncu - 1) / ncu) * 192;
   return cost192 < cost256 ? 3 : 0;
@@ -502,6 +509,7 @@ template <int FA, int FB, int OUT> static hipError_t launch_dma_family(const MmA
     case 0: return launch_dma<FA, FB, 256, 256, 2, 4, 1, OUT>(p, st);
     case 3: return launch_dma<FA, FB, 256, 192, 2, 4, 1, OUT>(p, st);
     case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2, OUT>(p, st);
+    case 5: return launch_dma<FA, FB, 64, 64, 1, 4, 2, OUT>(p, st);
     default: return launch_dma<FA, FB, 64, 128, 1, 4, 2, OUT>(p, st);
   }
 }
