@@ -2,6 +2,7 @@
 // the kernel launchers.  Every check runs before any HIP call, so a rejected
 // call has no side effects.
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -48,6 +49,14 @@ static bool valid_fmt(int f) { return f == FP8MI_E4M3 || f == FP8MI_E5M2; }
 static bool valid_dtype(int d) { return d == FP8MI_F32 || d == FP8MI_F16 || d == FP8MI_BF16; }
 static int dtype_bytes(int d) { return d == FP8MI_F32 ? 4 : 2; }
 
+// rows x ld elements of elem bytes stay within 2^62 bytes: no allocation is
+// that large, and the bound keeps every 64-bit index product in the kernels
+// (and the checks below) from overflowing.
+static bool span_ok(int64_t rows, int64_t ld, int64_t elem) {
+  if (rows <= 0 || ld <= 0) return true;
+  return ld <= (INT64_C(1) << 62) / elem / rows;
+}
+
 static fp8mi_status check_scale_ring(const float* scale, uint32_t* ring, int32_t H) {
   if ((scale == nullptr) == (ring == nullptr))
     return fail(FP8MI_ERR_ARG, "give exactly one of scale and ring (scale=%p ring=%p)", (const void*)scale,
@@ -64,6 +73,8 @@ static fp8mi_status check_input(const void* x, int dt, int64_t rows, int64_t col
   if (rows < 0 || cols < 0) return fail(FP8MI_ERR_SHAPE, "negative shape rows=%lld cols=%lld", (long long)rows,
                                         (long long)cols);
   if (rows > 0 && ld_x < cols) return fail(FP8MI_ERR_SHAPE, "ld_x %lld < cols %lld", (long long)ld_x, (long long)cols);
+  if (!span_ok(rows, ld_x, dtype_bytes(dt)))
+    return fail(FP8MI_ERR_SHAPE, "rows %lld x ld_x %lld beyond 2^62 bytes", (long long)rows, (long long)ld_x);
   if (rows > 0 && cols > 0 && x == nullptr) return fail(FP8MI_ERR_NULL, "x is NULL");
   if (reinterpret_cast<uintptr_t>(x) % dtype_bytes(dt)) return fail(FP8MI_ERR_ARG, "x not aligned to its element size");
   return FP8MI_OK;
@@ -83,6 +94,8 @@ static fp8mi_status check_outputs(int mode, int64_t rows, int64_t cols, const ui
     if (cols > 0 && ld_t < rows) return fail(FP8MI_ERR_SHAPE, "transposed ld %lld < rows %lld", (long long)ld_t,
                                              (long long)rows);
   }
+  if ((mode != 1 && !span_ok(rows, ld_row, 1)) || (mode != 0 && !span_ok(cols, ld_t, 1)))
+    return fail(FP8MI_ERR_SHAPE, "output extent beyond 2^62 bytes");
   if (reinterpret_cast<uintptr_t>(scale_inv_out) & 3u || reinterpret_cast<uintptr_t>(amax_out) & 3u)
     return fail(FP8MI_ERR_ARG, "fp32 scalars must be 4-byte aligned");
   return FP8MI_OK;
@@ -240,6 +253,12 @@ fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_
     return fail(FP8MI_ERR_SHAPE, "lda %lld / ldb %lld shorter than a stored row (%lld / %lld)", (long long)lda,
                 (long long)ldb, (long long)row_a, (long long)row_b);
   if (stride_a < 0 || stride_b < 0 || stride_c < 0) return fail(FP8MI_ERR_STRIDE, "negative batch stride");
+  const int64_t elem_c = fp8_out ? 1 : 2;
+  const bool reads = K > 0;  // A and B are not read when K = 0
+  if ((reads && (!span_ok((layout & 1) ? K : M, lda, 1) || !span_ok((layout & 2) ? K : N, ldb, 1) ||
+                 !span_ok(batch, stride_a, 1) || !span_ok(batch, stride_b, 1))) ||
+      !span_ok(M, ldc, elem_c) || !span_ok(batch, stride_c, elem_c))
+    return fail(FP8MI_ERR_SHAPE, "an operand or output extent is beyond 2^62 bytes");
   if (batch > 1 && stride_c < M * ldc)
     return fail(FP8MI_ERR_STRIDE, "stride_c %lld < M*ldc %lld: batches would overlap", (long long)stride_c,
                 (long long)(M * ldc));
@@ -255,8 +274,10 @@ fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_
     if ((stride_a % 16) || (stride_b % 16))
       return fail(FP8MI_ERR_UNSUPPORTED, "batch strides of a and b must be multiples of 16");
   }
-  if ((M + 63) / 64 > 65535 || batch > 65535)
-    return fail(FP8MI_ERR_UNSUPPORTED, "M=%lld / batch=%lld beyond the launch grid", (long long)M, (long long)batch);
+  // the smallest tile is 64 x 64: its count bounds every kernel's grid
+  if ((M + 63) / 64 > 65535 || batch > 65535 || (N + 63) / 64 > 0x7FFFFFFF / ((M + 63) / 64))
+    return fail(FP8MI_ERR_UNSUPPORTED, "M=%lld N=%lld batch=%lld beyond the launch grid", (long long)M, (long long)N,
+                (long long)batch);
   p.a = a; p.b = b; p.lda = lda; p.ldb = ldb; p.stride_a = stride_a; p.stride_b = stride_b;
   p.a_scale_inv = a_scale_inv; p.b_scale_inv = b_scale_inv;
   p.bias = bias; p.bias_dtype = bias ? bias_dtype : -1; p.bias_scale = bias_scale;
@@ -292,6 +313,8 @@ fp8mi_status fp8_bias_grad(const void* dy, int dy_dtype, int64_t rows, int64_t c
   if (!out) return fail(FP8MI_ERR_NULL, "out is NULL");
   if (rows > 0 && !dy) return fail(FP8MI_ERR_NULL, "dy is NULL");
   if (rows > 0 && ld < cols) return fail(FP8MI_ERR_SHAPE, "ld %lld < cols %lld", (long long)ld, (long long)cols);
+  if (!span_ok(rows, ld, 2)) return fail(FP8MI_ERR_SHAPE, "rows %lld x ld %lld beyond 2^62 bytes", (long long)rows,
+                                         (long long)ld);
   if (reinterpret_cast<uintptr_t>(dy) & 1u) return fail(FP8MI_ERR_ARG, "dy must be 2-byte aligned");
   fp8mi_status s = check_bias_grad(dy_dtype, rows, cols, out, workspace, workspace_bytes);
   if (s != FP8MI_OK) return s;

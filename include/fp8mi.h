@@ -10,6 +10,9 @@
  * buffer.  Arguments are checked before anything is launched: a call that
  * returns a status other than FP8MI_OK has written nothing.  A HIP launch
  * failure returns FP8MI_ERR_HIP; fp8mi_last_error() then holds the HIP text.
+ * Outputs must not overlap the inputs or each other (the results are then
+ * undefined).  An extent -- rows x leading dimension x element bytes, or
+ * batch x batch stride -- above 2^62 bytes is rejected with FP8MI_ERR_SHAPE.
  *
  * Citations are to the AstrAI commit-log pages (Gitea, ViperEkura/AstrAI);
  * "log:<path>" names the commit history page of that path.
@@ -95,7 +98,8 @@ typedef enum {
  * transposed quantize that handles odd widths and misaligned bases in-kernel).
  *
  *   x          device, element (i, j) at x[i * ld_x + j]; dtype x_dtype.
- *              Any element alignment; ld_x >= cols.
+ *              Any base aligned to the element size (no 16-byte
+ *              alignment needed); ld_x >= cols.
  *   fmt        FP8MI_E4M3 or FP8MI_E5M2.
  *   transposed 0: out[i * ld_out + j] = q(i, j), ld_out >= cols;
  *              1: out[j * ld_out + i] = q(i, j), ld_out >= rows.
@@ -188,7 +192,9 @@ FP8MI_API fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const flo
  * Requirements: a, b 16-byte aligned; lda, ldb, K multiples of 16 (else
  * FP8MI_ERR_UNSUPPORTED); lda, ldb >= K; ldc >= N; c 2-byte aligned; with
  * batch > 1, stride_c >= M * ldc.  M, N or batch 0: no-op.  K == 0 writes
- * bf16(bias) (or zeros).
+ * bf16(bias) (or zeros).  Launch-grid limits: ceil(M / 64) <= 65535,
+ * batch <= 65535 and ceil(M / 64) * ceil(N / 64) < 2^31 (else
+ * FP8MI_ERR_UNSUPPORTED).
  */
 FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a,
                     const uint8_t* b, int fmt_b, int64_t ldb, int64_t stride_b,

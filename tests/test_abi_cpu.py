@@ -62,6 +62,8 @@ def q(L, x=FAKE, dt=2, rows=4, cols=4, ld=4, fmt=0, tr=0, out=FAKE, ld_out=4, sc
     (dict(scale=None), ARG), (dict(ring=FAKE, H=4), ARG),
     (dict(scale=None, ring=FAKE, H=0), SHAPE), (dict(scale=None, ring=FAKE, H=5000), SHAPE),
     (dict(x=FAKE + 1), ARG), (dict(scale=FAKE + 2), ARG), (dict(amax=FAKE + 1), ARG),
+    # extents beyond 2^62 bytes
+    (dict(ld=1 << 61), SHAPE), (dict(ld_out=1 << 62), SHAPE), (dict(tr=1, ld_out=1 << 62), SHAPE),
 ])
 def test_quantize_rejects(L, kw, status):
     assert q(L, **kw) == status
@@ -139,6 +141,7 @@ def test_bias_grad_rejects(L):
     assert f(FAKE, 2, 4, 4, 4, FAKE, None, W, None) == NULL          # workspace missing
     assert f(FAKE, 2, 4, 4, 4, FAKE, FAKE, W - 1, None) == ARG       # workspace too small
     assert f(FAKE, 2, 4, 4, 4, FAKE, FAKE + 4, W, None) == ARG       # workspace misaligned
+    assert f(FAKE, 2, 4, 4, 1 << 61, FAKE, FAKE, W, None) == SHAPE  # rows x ld beyond 2^62 bytes
     assert f(None, 2, 4, 0, 4, None, None, 0, None) == OK            # no columns: no-op
 
 
@@ -234,6 +237,13 @@ def test_mm_ex_rejects(L):
     assert call(lay=1, M=64, lda=48) == SHAPE         # K-major A: lda must cover M
     assert call(lay=2, N=64, ldb=48) == SHAPE
     assert call(lay=1, M=64, lda=72) == UNSUP         # lda % 16
+    # extents beyond 2^62 bytes and grids beyond the launch limits are refused
+    big = 1 << 61
+    assert call(lda=big) == SHAPE                     # M x lda
+    assert call(ldc=big) == SHAPE                     # M x ldc x 2 bytes
+    assert call(batch=4, sa=big) == SHAPE             # batch x stride_a
+    assert call(lay=1, M=64, lda=big - big % 16) == SHAPE   # K-major A: K x lda
+    assert call(M=1 << 20, N=1 << 24, ldc=1 << 24) == UNSUP  # 2^32 tiles of 64 x 64
     # the plain fp8_mm refuses an fp8 bias type (it has no bias scale)
     assert L.fp8_mm(FAKE, 0, 32, 0, FAKE, 0, 32, 0, 4, 4, 32, 1, None, None, FAKE, 3, FAKE, 4, 16, None) == ENUM
 
