@@ -67,8 +67,72 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _as_codes(t: torch.Tensor) -> torch.Tensor:
+def _as_codes(t: torch.Tensor, name: str = "codes") -> torch.Tensor:
+    if t.element_size() != 1:
+        raise ValueError(f"{name} must hold 1-byte fp8 codes, got {t.dtype}")
     return t.view(torch.uint8) if t.dtype != torch.uint8 else t
+
+
+# Argument checks.  The library takes raw device pointers and sizes, so the
+# binding checks what only the tensors know -- device, dtype, shape -- before
+# the call; the library itself checks sizes, strides and alignment.
+
+def _on_device(*ts) -> None:
+    """Every tensor argument lives on the current HIP device (the library
+    launches there): a host tensor or another device's memory would be read
+    as this device's."""
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        d = t.get_device()
+        if d < 0:
+            raise ValueError("tensor arguments must be HIP device tensors, got a host tensor")
+        if dev is None:
+            dev = d
+        elif d != dev:
+            raise ValueError(f"tensor arguments on devices cuda:{dev} and cuda:{d}")
+    if dev is not None and dev != torch.cuda.current_device():
+        raise ValueError(f"tensors on cuda:{dev} but the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _dt(t: torch.Tensor, name: str) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise ValueError(f"{name} must be float32, float16 or bfloat16, got {t.dtype}") from None
+
+
+def _scalar(t, name: str) -> None:
+    """A device fp32 scalar argument (its first element is read or written)."""
+    if t is not None and (t.dtype != torch.float32 or t.numel() < 1):
+        raise ValueError(f"{name} must be a float32 tensor of at least one element")
+
+
+def _matrix_out(t: torch.Tensor, shape, name: str) -> None:
+    """A 2-D output of exactly `shape` with unit stride along its rows."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} needs unit stride along its rows")
+
+
+def _vector(t: torch.Tensor, n: int, name: str) -> None:
+    """A contiguous 1-D tensor of n elements."""
+    if t.dim() != 1 or t.numel() != n or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous 1-D tensor of {n} elements, got {tuple(t.shape)}")
+
+
+def _quant_checks(x, name, out_row, out_t, scale, scale_inv_out, amax_out):
+    rows, cols = x.shape
+    if out_row is not None:
+        _matrix_out(out_row, (rows, cols), "out" if out_t is None else "out_row")
+    if out_t is not None:
+        _matrix_out(out_t, (cols, rows), "out" if out_row is None else "out_t")
+    _scalar(scale, "scale")
+    _scalar(scale_inv_out, "scale_inv_out")
+    _scalar(amax_out, "amax_out")
+    return _dt(x, name)
 
 
 def _ring_args(ring):
@@ -116,11 +180,14 @@ def fp8_quantize(x: torch.Tensor, fmt, transposed: bool = False, out: torch.Tens
     f = _fmt(fmt)
     if out is None:
         out = torch.empty((cols, rows) if transposed else (rows, cols), dtype=torch.uint8, device=x.device)
-    out = _as_codes(out)
+    out = _as_codes(out, "out")
+    dt = _quant_checks(x, "x", None if transposed else out, out if transposed else None, scale, scale_inv_out,
+                       amax_out)
     ld_x = x.stride(0) if rows > 1 else cols
     ld_out = out.stride(0) if out.shape[0] > 1 else out.shape[1]
     rp, h = _ring_args(ring)
-    _check(lib().fp8_quantize(_ptr(x), _DT[x.dtype], rows, cols, ld_x, f, int(bool(transposed)), _ptr(out),
+    _on_device(x, out, scale, ring, scale_inv_out, amax_out)
+    _check(lib().fp8_quantize(_ptr(x), dt, rows, cols, ld_x, f, int(bool(transposed)), _ptr(out),
                               ld_out, _ptr(scale), rp, h, _ptr(scale_inv_out), _ptr(amax_out), _stream(x)))
     return out
 
@@ -137,12 +204,14 @@ def fp8_quantize_dual(x: torch.Tensor, fmt, out_row: torch.Tensor | None = None,
         out_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if out_t is None:
         out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
-    out_row, out_t = _as_codes(out_row), _as_codes(out_t)
+    out_row, out_t = _as_codes(out_row, "out_row"), _as_codes(out_t, "out_t")
+    dt = _quant_checks(x, "x", out_row, out_t, scale, scale_inv_out, amax_out)
     ld_x = x.stride(0) if rows > 1 else cols
     ld_r = out_row.stride(0) if out_row.shape[0] > 1 else out_row.shape[1]
     ld_t = out_t.stride(0) if out_t.shape[0] > 1 else out_t.shape[1]
     rp, h = _ring_args(ring)
-    _check(lib().fp8_quantize_dual(_ptr(x), _DT[x.dtype], rows, cols, ld_x, f, _ptr(out_row), ld_r, _ptr(out_t),
+    _on_device(x, out_row, out_t, scale, ring, scale_inv_out, amax_out)
+    _check(lib().fp8_quantize_dual(_ptr(x), dt, rows, cols, ld_x, f, _ptr(out_row), ld_r, _ptr(out_t),
                                    ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out), _ptr(amax_out), _stream(x)))
     return out_row, out_t
 
@@ -167,12 +236,17 @@ def fp8_quantize_dual_bias_grad(dy: torch.Tensor, fmt, out_row: torch.Tensor | N
     need = fp8_bias_grad_workspace_bytes(rows, cols)
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dy.device)
-    out_row, out_t = _as_codes(out_row), _as_codes(out_t)
+    out_row, out_t = _as_codes(out_row, "out_row"), _as_codes(out_t, "out_t")
+    dt = _quant_checks(dy, "dy", out_row, out_t, scale, scale_inv_out, amax_out)
+    _vector(bias_grad_out, cols, "bias_grad_out")
+    if bias_grad_out.dtype != torch.bfloat16:
+        raise ValueError("bias_grad_out must be bfloat16")
     ld_x = dy.stride(0) if rows > 1 else cols
     ld_r = out_row.stride(0) if out_row.shape[0] > 1 else out_row.shape[1]
     ld_t = out_t.stride(0) if out_t.shape[0] > 1 else out_t.shape[1]
     rp, h = _ring_args(ring)
-    _check(lib().fp8_quantize_dual_bias_grad(_ptr(dy), _DT[dy.dtype], rows, cols, ld_x, f, _ptr(out_row), ld_r,
+    _on_device(dy, out_row, out_t, scale, ring, scale_inv_out, amax_out, bias_grad_out, workspace)
+    _check(lib().fp8_quantize_dual_bias_grad(_ptr(dy), dt, rows, cols, ld_x, f, _ptr(out_row), ld_r,
                                              _ptr(out_t), ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out),
                                              _ptr(amax_out), _ptr(bias_grad_out), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(dy)))
@@ -197,12 +271,15 @@ def fp8_quantize_dynamic(x: torch.Tensor, fmt, layout: int = LAYOUT_ROW, out_row
         out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
     if workspace is None:
         workspace = torch.empty(DYNAMIC_WORKSPACE_BYTES, dtype=torch.uint8, device=x.device)
-    out_row = None if out_row is None else _as_codes(out_row)
-    out_t = None if out_t is None else _as_codes(out_t)
+    out_row = None if out_row is None else _as_codes(out_row, "out_row")
+    out_t = None if out_t is None else _as_codes(out_t, "out_t")
+    dt = _quant_checks(x, "x", out_row if layout != LAYOUT_T else None, out_t if layout != LAYOUT_ROW else None,
+                       None, scale_inv_out, amax_out)
+    _on_device(x, out_row, out_t, scale_inv_out, amax_out, workspace)
     ld_x = x.stride(0) if rows > 1 else cols
     ld_r = 0 if out_row is None else (out_row.stride(0) if out_row.shape[0] > 1 else out_row.shape[1])
     ld_t = 0 if out_t is None else (out_t.stride(0) if out_t.shape[0] > 1 else out_t.shape[1])
-    _check(lib().fp8_quantize_dynamic(_ptr(x), _DT[x.dtype], rows, cols, ld_x, f, layout, _ptr(out_row), ld_r,
+    _check(lib().fp8_quantize_dynamic(_ptr(x), dt, rows, cols, ld_x, f, layout, _ptr(out_row), ld_r,
                                       _ptr(out_t), ld_t, _ptr(scale_inv_out), _ptr(amax_out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(x)))
     return out_row, out_t
@@ -212,6 +289,8 @@ def fp8_amax_fold(ring: torch.Tensor, amax: torch.Tensor, fmt) -> None:
     """Fold a device fp32 amax into the ring (the fold a ring-mode quantize
     performs in its last workgroup)."""
     rp, h = _ring_args(ring)
+    _scalar(amax, "amax")
+    _on_device(ring, amax)
     _check(lib().fp8_amax_fold(rp, h, _ptr(amax), _fmt(fmt), _stream(ring)))
 
 
@@ -258,7 +337,9 @@ def _operand_ld(t3: torch.Tensor, name: str):
 
 def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_scale, out, out_fmt,
              out_scale=None, out_ring=None, out_scale_inv=None, out_amax=None, ex=True):
-    a, b = _as_codes(a), _as_codes(b)
+    a, b = _as_codes(a, "a"), _as_codes(b, "b")
+    if a.dim() not in (2, 3) or b.dim() not in (2, 3):
+        raise ValueError("a and b must be [M, K] / [N, K] or batched [batch, M, K] / [batch, N, K]")
     a3 = a if a.dim() == 3 else a.unsqueeze(0)
     b3 = b if b.dim() == 3 else b.unsqueeze(0)
     if a3.shape[-1] != b3.shape[-1]:
@@ -278,16 +359,28 @@ def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_
         shape = (batch, M, N) if (a.dim() == 3 or b.dim() == 3) else (M, N)
         out = torch.empty(shape, dtype=torch.bfloat16 if c_dt == BF16 else torch.uint8, device=a.device)
     if c_dt != BF16:
-        out = _as_codes(out)
+        out = _as_codes(out, "out")
+    elif out.dtype != torch.bfloat16:
+        raise ValueError(f"out must be bfloat16, got {out.dtype}")
     c3 = out if out.dim() == 3 else out.unsqueeze(0)
+    if tuple(c3.shape) != (batch, M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(batch, M, N) if batch > 1 else (M, N)}")
+    if N > 1 and c3.stride(2) != 1:
+        raise ValueError("out needs unit stride along N")
     ldc = c3.stride(1) if M > 1 else N
     sc = c3.stride(0) if batch > 1 else M * ldc
     if bias is None:
         bias_dt = 0
     elif bias_fmt is not None:
-        bias, bias_dt = _as_codes(bias), FP8_E4M3 + _fmt(bias_fmt)
+        bias, bias_dt = _as_codes(bias, "bias"), FP8_E4M3 + _fmt(bias_fmt)
     else:
-        bias_dt = _DT[bias.dtype]
+        bias_dt = _dt(bias, "bias")
+    if bias is not None:
+        _vector(bias, N, "bias")
+    for t, name in ((a_scale_inv, "a_scale_inv"), (b_scale_inv, "b_scale_inv"), (bias_scale, "bias_scale"),
+                    (out_scale, "out_scale"), (out_scale_inv, "out_scale_inv"), (out_amax, "out_amax")):
+        _scalar(t, name)
+    _on_device(a3, b3, a_scale_inv, b_scale_inv, bias, bias_scale, out, out_scale, out_ring, out_scale_inv, out_amax)
     if not ex and layout == 0:
         _check(lib().fp8_mm(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
                             _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(out), ldc, sc,
@@ -323,8 +416,13 @@ def fp8_bias_grad(dy: torch.Tensor, out: torch.Tensor | None = None,
     need = fp8_bias_grad_workspace_bytes(rows, cols)
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dy.device)
+    dt = _dt(dy, "dy")
+    _vector(out, cols, "out")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    _on_device(d2, out, workspace)
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().fp8_bias_grad(_ptr(d2), _DT[dy.dtype], rows, cols, ld, _ptr(out), _ptr(workspace), nbytes,
+    _check(lib().fp8_bias_grad(_ptr(d2), dt, rows, cols, ld, _ptr(out), _ptr(workspace), nbytes,
                                _stream(dy)))
     return out
 
@@ -333,4 +431,6 @@ def fp8_ring_seed(ring: torch.Tensor, amax: torch.Tensor, fmt) -> None:
     """Reset a ring and publish the scale a fold of `amax` into an empty
     window gives (fmt_max / amax, or 1.0)."""
     rp, h = _ring_args(ring)
+    _scalar(amax, "amax")
+    _on_device(ring, amax)
     _check(lib().fp8_ring_seed(rp, h, _ptr(amax), _fmt(fmt), _stream(ring)))

@@ -120,6 +120,42 @@ def test_binding_raises_without_gpu_on_bad_args():
         fp8mi.fp8_quantize(x, "e9m9", scale=None)
 
 
+def test_binding_checks_tensor_arguments():
+    """The binding refuses, before any library call, what only the tensors
+    know: host tensors, wrong output shapes, non-code operands, wrong dtypes
+    and bias lengths (host-side logic only: CPU tensors, nothing launched)."""
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    one = torch.ones(1)
+    codes = torch.zeros(4, 8, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):                       # host tensors
+        fp8mi.fp8_quantize(x, fp8mi.E4M3, scale=one)
+    with pytest.raises(ValueError, match="shape"):                        # out of the wrong shape
+        fp8mi.fp8_quantize(x, fp8mi.E4M3, out=torch.zeros(2, 8, dtype=torch.uint8), scale=one)
+    with pytest.raises(ValueError, match="shape"):                        # transposed out is [cols, rows]
+        fp8mi.fp8_quantize(x, fp8mi.E4M3, True, out=torch.zeros(4, 8, dtype=torch.uint8), scale=one)
+    with pytest.raises(ValueError, match="shape"):
+        fp8mi.fp8_quantize_dual(x, fp8mi.E4M3, out_t=torch.zeros(4, 8, dtype=torch.uint8), scale=one)
+    with pytest.raises(ValueError, match="float32"):                      # scale of the wrong dtype
+        fp8mi.fp8_quantize(x, fp8mi.E4M3, scale=torch.ones(1, dtype=torch.float64))
+    with pytest.raises(ValueError, match="float32, float16 or bfloat16"):  # integer input
+        fp8mi.fp8_quantize(x.to(torch.int16), fp8mi.E4M3, scale=one)
+    with pytest.raises(ValueError, match="1-byte"):                       # bf16 passed as fp8 codes
+        fp8mi.fp8_mm(x, codes)
+    with pytest.raises(ValueError, match="shape"):                        # 2-D out for a batch of 3
+        fp8mi.fp8_mm(codes.expand(3, 4, 8), codes, out=torch.zeros(4, 4, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="bfloat16"):
+        fp8mi.fp8_mm(codes, codes, out=torch.zeros(4, 4))
+    with pytest.raises(ValueError, match="bias"):                         # bias of the wrong length
+        fp8mi.fp8_mm(codes, codes, bias=torch.zeros(5))
+    with pytest.raises(ValueError, match="device"):                       # valid shapes, host tensors
+        fp8mi.fp8_mm(codes, codes, bias=torch.zeros(4))
+    with pytest.raises(ValueError, match="bias_grad_out"):
+        fp8mi.fp8_quantize_dual_bias_grad(x, fp8mi.E5M2, scale=one, bias_grad_out=torch.zeros(7, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out"):
+        fp8mi.fp8_bias_grad(x, out=torch.zeros(8))
+
+
 def test_bias_grad_workspace_bytes(L):
     f = L.fp8_bias_grad_workspace_bytes
     assert f(0, 16) == 0 and f(16, 0) == 0 and f(-1, 4) == 0
