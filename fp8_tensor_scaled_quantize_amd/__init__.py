@@ -57,6 +57,13 @@ def _ptr(t):
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_raw_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def _current_device() -> int:
+    """torch's current HIP device (the raw getter skips the lazy-init check,
+    done already by the time a device tensor exists)."""
+    return _raw_device() if _raw_device is not None else torch.cuda.current_device()
 
 
 def _stream(t: torch.Tensor):
@@ -92,8 +99,8 @@ def _on_device(*ts) -> None:
             dev = d
         elif d != dev:
             raise ValueError(f"tensor arguments on devices cuda:{dev} and cuda:{d}")
-    if dev is not None and dev != torch.cuda.current_device():
-        raise ValueError(f"tensors on cuda:{dev} but the current device is cuda:{torch.cuda.current_device()}")
+    if dev is not None and dev != _current_device():
+        raise ValueError(f"tensors on cuda:{dev} but the current device is cuda:{_current_device()}")
 
 
 def _dt(t: torch.Tensor, name: str) -> int:
@@ -111,7 +118,7 @@ def _scalar(t, name: str) -> None:
 
 def _matrix_out(t: torch.Tensor, shape, name: str) -> None:
     """A 2-D output of exactly `shape` with unit stride along its rows."""
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} needs unit stride along its rows")
@@ -318,57 +325,71 @@ def fp8_mm_ex(a: torch.Tensor, b: torch.Tensor, fmt_a=E4M3, fmt_b=E4M3, a_scale_
                     out_scale, out_ring, out_scale_inv, out_amax)
 
 
-def _operand_ld(t3: torch.Tensor, name: str):
-    """Leading dimension of a [batch, rows, K] operand and whether it is
-    K-major (a transposed view of [K, rows] storage: unit stride along rows),
-    which the library reads through the FP8MI_A_KM / FP8MI_B_KM layout tags."""
-    rows, K = t3.shape[1], t3.shape[2]
-    if K <= 1 or t3.stride(2) == 1:
-        return (t3.stride(1) if rows > 1 else K), False
-    if rows <= 1 or t3.stride(1) == 1:
-        ld = t3.stride(2) if K > 1 else rows
+def _operand(t: torch.Tensor, name: str):
+    """(batch, rows, K, batch stride, leading dimension, K-major) of a
+    [rows, K] or [batch, rows, K] operand.  An operand that is a transposed
+    view of [K, rows] storage (unit stride along its rows) is K-major: the
+    library reads it through the FP8MI_A_KM / FP8MI_B_KM layout tags."""
+    if t.dim() == 3:
+        batch, rows, K = t.shape
+        sb, sr, sk = t.stride()
+    elif t.dim() == 2:
+        batch, (rows, K), sb = 1, t.shape, 0
+        sr, sk = t.stride()
+    else:
+        raise ValueError(f"operand {name} must be [rows, K] or [batch, rows, K], got {tuple(t.shape)}")
+    if batch == 1:
+        sb = 0
+    if K <= 1 or sk == 1:
+        return batch, rows, K, sb, (sr if rows > 1 else K), False
+    if rows <= 1 or sr == 1:
+        ld = sk
         # the library reads K full rows of ld bytes (the last row's padding included)
-        last = t3.storage_offset() + (t3.shape[0] - 1) * t3.stride(0) + K * ld
-        if last > t3.untyped_storage().nbytes():
+        last = t.storage_offset() + (batch - 1) * sb + K * ld
+        if last > t.untyped_storage().nbytes():
             raise ValueError(f"K-major operand {name} must span {K} full rows of {ld} bytes in its storage")
-        return ld, True
+        return batch, rows, K, sb, ld, True
     raise ValueError(f"operand {name} needs unit stride along K or along its rows")
+
+
+def _operand_ld(t: torch.Tensor, name: str):
+    """Leading dimension of an operand and whether it is K-major."""
+    return _operand(t, name)[4:]
 
 
 def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_scale, out, out_fmt,
              out_scale=None, out_ring=None, out_scale_inv=None, out_amax=None, ex=True):
     a, b = _as_codes(a, "a"), _as_codes(b, "b")
-    if a.dim() not in (2, 3) or b.dim() not in (2, 3):
-        raise ValueError("a and b must be [M, K] / [N, K] or batched [batch, M, K] / [batch, N, K]")
-    a3 = a if a.dim() == 3 else a.unsqueeze(0)
-    b3 = b if b.dim() == 3 else b.unsqueeze(0)
-    if a3.shape[-1] != b3.shape[-1]:
+    ba, M, K, sa, lda, a_km = _operand(a, "a")
+    bb, N, Kb, sb, ldb, b_km = _operand(b, "b")
+    if K != Kb:
         raise ValueError(f"K mismatch: {tuple(a.shape)} vs {tuple(b.shape)}")
-    batch = max(a3.shape[0], b3.shape[0])
-    if a3.shape[0] not in (1, batch) or b3.shape[0] not in (1, batch):
+    batch = ba if ba > 1 else bb
+    if ba not in (1, batch) or bb not in (1, batch):
         raise ValueError("batch sizes must match or be 1")
-    M, K = a3.shape[1], a3.shape[2]
-    N = b3.shape[1]
-    lda, a_km = _operand_ld(a3, "a")
-    ldb, b_km = _operand_ld(b3, "b")
     layout = (1 if a_km else 0) | (2 if b_km else 0)
-    sa = 0 if a3.shape[0] == 1 else a3.stride(0)
-    sb = 0 if b3.shape[0] == 1 else b3.stride(0)
     c_dt = BF16 if out_fmt is None else FP8_E4M3 + _fmt(out_fmt)
+    batched = a.dim() == 3 or b.dim() == 3
     if out is None:
-        shape = (batch, M, N) if (a.dim() == 3 or b.dim() == 3) else (M, N)
-        out = torch.empty(shape, dtype=torch.bfloat16 if c_dt == BF16 else torch.uint8, device=a.device)
+        out = torch.empty((batch, M, N) if batched else (M, N), dtype=torch.bfloat16 if c_dt == BF16 else torch.uint8,
+                          device=a.device)
     if c_dt != BF16:
         out = _as_codes(out, "out")
     elif out.dtype != torch.bfloat16:
         raise ValueError(f"out must be bfloat16, got {out.dtype}")
-    c3 = out if out.dim() == 3 else out.unsqueeze(0)
-    if tuple(c3.shape) != (batch, M, N):
+    if out.dim() == 3:
+        cshape, (sc, ldc, scn) = tuple(out.shape), out.stride()
+    else:
+        cshape, (ldc, scn) = (1,) + tuple(out.shape), out.stride()
+        sc = M * ldc
+    if cshape != (batch, M, N):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(batch, M, N) if batch > 1 else (M, N)}")
-    if N > 1 and c3.stride(2) != 1:
+    if N > 1 and scn != 1:
         raise ValueError("out needs unit stride along N")
-    ldc = c3.stride(1) if M > 1 else N
-    sc = c3.stride(0) if batch > 1 else M * ldc
+    if M <= 1:
+        ldc = N
+    if batch <= 1:
+        sc = M * ldc
     if bias is None:
         bias_dt = 0
     elif bias_fmt is not None:
@@ -377,19 +398,27 @@ def _mm_call(a, b, fmt_a, fmt_b, a_scale_inv, b_scale_inv, bias, bias_fmt, bias_
         bias_dt = _dt(bias, "bias")
     if bias is not None:
         _vector(bias, N, "bias")
-    for t, name in ((a_scale_inv, "a_scale_inv"), (b_scale_inv, "b_scale_inv"), (bias_scale, "bias_scale"),
-                    (out_scale, "out_scale"), (out_scale_inv, "out_scale_inv"), (out_amax, "out_amax")):
-        _scalar(t, name)
-    _on_device(a3, b3, a_scale_inv, b_scale_inv, bias, bias_scale, out, out_scale, out_ring, out_scale_inv, out_amax)
+    _scalar(a_scale_inv, "a_scale_inv")
+    _scalar(b_scale_inv, "b_scale_inv")
+    if ex:
+        for t, name in ((bias_scale, "bias_scale"), (out_scale, "out_scale"), (out_scale_inv, "out_scale_inv"),
+                        (out_amax, "out_amax")):
+            _scalar(t, name)
+        _on_device(a, b, a_scale_inv, b_scale_inv, bias, bias_scale, out, out_scale, out_ring, out_scale_inv,
+                   out_amax)
+    else:
+        _on_device(a, b, a_scale_inv, b_scale_inv, bias, out)
+    L = lib()
     if not ex and layout == 0:
-        _check(lib().fp8_mm(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch,
-                            _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(out), ldc, sc,
-                            _stream(a)))
+        _check(L.fp8_mm(a.data_ptr(), _fmt(fmt_a), lda, sa, b.data_ptr(), _fmt(fmt_b), ldb, sb, M, N, K, batch,
+                        _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, out.data_ptr(), ldc, sc,
+                        _stream(a)))
         return out
     rp, h = _ring_args(out_ring)
-    _check(lib().fp8_mm_ex(_ptr(a3), _fmt(fmt_a), lda, sa, _ptr(b3), _fmt(fmt_b), ldb, sb, M, N, K, batch, layout,
-                           _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(bias_scale), _ptr(out),
-                           c_dt, ldc, sc, _ptr(out_scale), rp, h, _ptr(out_scale_inv), _ptr(out_amax), _stream(a)))
+    _check(L.fp8_mm_ex(a.data_ptr(), _fmt(fmt_a), lda, sa, b.data_ptr(), _fmt(fmt_b), ldb, sb, M, N, K, batch,
+                       layout, _ptr(a_scale_inv), _ptr(b_scale_inv), _ptr(bias), bias_dt, _ptr(bias_scale),
+                       out.data_ptr(), c_dt, ldc, sc, _ptr(out_scale), rp, h, _ptr(out_scale_inv), _ptr(out_amax),
+                       _stream(a)))
     return out
 
 
