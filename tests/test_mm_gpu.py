@@ -226,3 +226,34 @@ def test_exact_integer_data(case):
     rows = sample_rows(M, 96, 70, key, 3)
     bias = O.widen_to_f32(synth.f32_to_bf16_bits(bias_v), "bf16").astype(np.float64) if with_bias else None
     check(np_bf16_bits(y), a, fa, b, fb, sa, sb, bias, rows, tag=f"exact {case}", exact=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(192, 160, 256), (4096, 4096, 256)], ids=["small-tiles", "256-tiles"])
+def test_nan_and_inf_codes_propagate(M, N, K):
+    """NaN and infinity codes reach the GEMM when the quantized tensor held
+    them.  E4M3 A (NaN 0x7F / 0xFF planted in two rows) times E5M2 B (+inf
+    0x7C, -inf 0xFC and NaN 0x7E planted in four columns), exact small-integer
+    data elsewhere: every output is NaN exactly where the oracle's float64
+    GEMM is (a NaN operand, 0 x inf, inf - inf), infinities match in sign,
+    and every finite output is bit-exact."""
+    a = make_int_codes((M, K), O.E4M3, 71, 1)
+    b = make_int_codes((N, K), O.E5M2, 71, 2)
+    a[5, 17], a[M - 3, K - 1] = 0x7F, 0xFF              # two NaN rows
+    a[:, 40] = np.where(np.arange(M) % 7 == 0, 0x00, a[:, 40])  # zeros meet b's +inf: NaN there
+    b[7, 40] = 0x7C                                      # column 7: a[i,40] * +inf
+    b[9, 3], b[9, 100] = 0xFC, 0x7C                      # column 9: -inf and +inf terms
+    b[11, 50] = 0x7E                                     # column 11: NaN
+    b[N - 1, 0] = 0xFC                                   # last column: -inf
+    bias = synth.rng(71, 3).integers(-8, 9, size=N).astype(np.float64)
+    sa, sb = 0.5, 2.0
+    y = fp8mi.fp8_mm(to_dev_codes(a), to_dev_codes(b), FID[O.E4M3], FID[O.E5M2], scalar(sa), scalar(sb),
+                     torch.from_numpy(bias.astype(np.float32)).to(DEV))
+    got = np_bf16_bits(y)
+    with np.errstate(invalid="ignore"):                 # 0 x inf and inf - inf are the point
+        ref, _ = O.mm(a, O.E4M3, b, O.E5M2, sa, sb, bias)
+    ref = ref[0]
+    gv, rv = O.bf16_bits_to_f64(got), O.bf16_bits_to_f64(ref)
+    assert np.isnan(rv[5]).all() and np.isnan(rv[:, 11]).all() and np.isinf(rv[:, N - 1]).any()
+    assert np.array_equal(np.isnan(gv), np.isnan(rv)), f"{(np.isnan(gv) != np.isnan(rv)).sum()} NaN positions differ"
+    fin = ~np.isnan(rv)
+    assert np.array_equal(got[fin], ref[fin]), f"{(got[fin] != ref[fin]).sum()} non-NaN outputs differ"
