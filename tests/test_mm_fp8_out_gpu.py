@@ -243,3 +243,39 @@ def test_fp8_bias_with_bf16_output_and_every_code():
     want, _ = O.mm(np.zeros((4, 0), np.uint8), O.E4M3, np.zeros((N, 0), np.uint8), O.E4M3, 1.0, 1.0,
                    O.dequant_bias(codes, O.E5M2, 0.375).astype(np.float64))
     assert np.array_equal(np_bf16_bits(y), want[0])
+
+
+def test_nan_and_inf_outputs_quantize():
+    """A GEMM whose outputs hold NaN (a NaN row of A, 0 x inf) and +-inf
+    (an infinity column of B), quantized to E4M3 with a ring: NaN outputs get
+    the NaN code (its sign bit is not compared: the sign of a NaN produced by
+    arithmetic is unspecified), infinities saturate to +-448, amax ignores
+    NaN and is inf, and the fold of an infinite amax publishes scale 1.0 --
+    all as the oracle's quantize of fl32(y); finite codes bit-exact."""
+    M, N, K = 192, 160, 256
+    a = make_int_codes((M, K), O.E4M3, 72, 1)
+    b = make_int_codes((N, K), O.E5M2, 72, 2)
+    a[5, 17] = 0x7F                                      # NaN row
+    a[:, 40] = np.where(np.arange(M) % 7 == 0, 0x00, a[:, 40])
+    b[7, 40] = 0x7C                                      # +inf column (NaN where a[i,40] = 0)
+    b[N - 1, 0] = 0xFC                                   # -inf column
+    sa, sb = 0.5, 2.0
+    ring0 = O.Ring.new(4, 1.0)
+    ring0.hist[:] = [3.0, 0.0, 1.0, 0.0]
+    ring0.scale, ring0.idx = np.float32(O.FMT_MAX[O.E4M3] / 4096.0), 1   # 7 * 2^-6: exact products
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = O.mm_quantized(a, O.E4M3, b, O.E5M2, O.E4M3, sa, sb, None, ring=ring0)
+    assert np.isinf(ref["amax"]) and ref["ring"].scale == np.float32(1.0)
+    ring = ring_from_oracle(ring0)
+    sinv_t, amax_t = scalar(-1), scalar(-1)
+    out = fp8mi.fp8_mm_ex(to_dev_codes(a), to_dev_codes(b), 0, 1, scalar(sa), scalar(sb), out_fmt=FID[O.E4M3],
+                          out_ring=ring, out_scale_inv=sinv_t, out_amax=amax_t)
+    torch.cuda.synchronize()
+    got, want = out.cpu().numpy(), ref["codes"].reshape(M, N)
+    nan = (want & 0x7F) == 0x7F
+    assert nan[5].all() and nan[:, 7].any() and not nan.all()
+    assert np.array_equal((got & 0x7F) == 0x7F, nan), "NaN codes at different positions"
+    assert np.array_equal(got[~nan], want[~nan]), f"{(got[~nan] != want[~nan]).sum()} non-NaN codes differ"
+    assert (want[~nan] == 0x7E).any() and (want[~nan] == 0xFE).any()      # both saturations occur
+    assert f32_bits(amax_t) == as_bits(ref["amax"]) and f32_bits(sinv_t) == as_bits(ref["scale_inv"])
+    assert np.array_equal(ring_state_words(ring), ref["ring"].words())
