@@ -43,6 +43,12 @@ adding the FP8-in/FP8-out GEMM):
   quantized in the GEMM epilogue with the layer's output ring ring_y;
   forward accepts such codes as x (x_scale_inv given) -- inference chaining
   with no quantize between layers.
+
+fp8_linear(x, layer) records one forward on torch's autograd tape
+(log:tests/extension, the commit giving the fp8 linear's forward/backward
+pair to an autograd function whose backward reads only its context and masks
+the gradients by needs_input_grad): loss.backward() then runs the layer's
+backward and leaves dX in x.grad, dW in weight.grad and db in bias.grad.
 """
 from __future__ import annotations
 
@@ -82,6 +88,7 @@ class Fp8Linear:
         self._amax = torch.empty(1, dtype=torch.float32, device=dev)
         self._one = torch.ones(1, dtype=torch.float32, device=dev)
         self._saved = None
+        self._forwards = 0  # forwards saved for backward so far (fp8_linear's pairing check)
 
     @classmethod
     def from_fp8_weight(cls, codes: torch.Tensor, scale_inv: torch.Tensor, bias: torch.Tensor | None = None,
@@ -156,6 +163,7 @@ class Fp8Linear:
             xq, xq_t = self._quantize_x(x2, save_for_backward)
         wq, wq_t = self._quantize_w(save_for_backward)
         self._saved = (xq_t, wq_t, x.shape) if save_for_backward else None
+        self._forwards += 1 if save_for_backward else 0
         self.last_codes = (xq, wq)
         out_shape = (*x.shape[:-1], self.weight.shape[0])
         if out_fp8 or self.bias_fmt is not None:
@@ -184,3 +192,35 @@ class Fp8Linear:
         dw = fp8_mm(gq_t, xq_t, E5M2, E4M3, sg, sx)
         self.last_grad_codes = (gq, gq_t)
         return dx.reshape(x_shape), dw, db
+
+
+class _Fp8LinearFn(torch.autograd.Function):
+    """One Fp8Linear step on torch's autograd tape.  The layer keeps a single
+    forward's saved codes and scale snapshots, so a backward must belong to
+    the layer's latest saved forward."""
+
+    @staticmethod
+    def forward(ctx, x, weight, bias, layer):
+        y = layer.forward(x, save_for_backward=True)
+        ctx.layer, ctx.step = layer, layer._forwards
+        ctx.dtypes = (x.dtype, weight.dtype, None if bias is None else bias.dtype)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        layer = ctx.layer
+        if layer._forwards != ctx.step:
+            raise RuntimeError("fp8_linear: the layer ran another forward since the one being differentiated")
+        dx, dw, db = layer.backward(dy.contiguous())
+        tx, tw, tb = ctx.dtypes
+        need = ctx.needs_input_grad
+        return (dx.to(tx) if need[0] else None, dw.to(tw) if need[1] else None,
+                db.to(tb) if need[2] and db is not None else None, None)
+
+
+def fp8_linear(x: torch.Tensor, layer: Fp8Linear) -> torch.Tensor:
+    """y = layer.forward(x) recorded for autograd: the backward pass runs
+    layer.backward (dY quantized with the layer's gradient ring, the dX and
+    dW GEMMs with the forward's scales, the fused bias gradient) and returns
+    dX, dW and db to x, layer.weight and layer.bias."""
+    return _Fp8LinearFn.apply(x, layer.weight, layer.bias, layer)
