@@ -16,6 +16,9 @@ not list still meet the bar.
   K-major with probability 1/3, E4M3 / E5M2 operands, no / f32 / f16 / bf16
   bias, a bf16 output with a padded ldc.  Small-integer data and power-of-two
   scales make every partial sum exact, so every output is bit-exact.
+* quantizing epilogue (60 cases): NT operands as above, E4M3 / E5M2 output
+  codes with an explicit scale or a ring, no / bf16 / fp8-stored bias; codes,
+  amax, scale_inv and ring words bit-exact.
 """
 import numpy as np
 import pytest
@@ -146,3 +149,58 @@ def test_random_gemm(i):
     got = y.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
     check(got, a if ba > 1 or batch > 1 else a[0], c["fa"], b if bb > 1 or batch > 1 else b[0], c["fb"], sa, sb,
           bias_np, tag=str(c), exact=True)
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_random_gemm_fp8_out(i):
+    """The quantizing epilogue on random cases: NT operands (as above, no
+    K-major: an fp8 output takes NT operands), E4M3 / E5M2 output codes with an
+    explicit scale or a ring holding a random history, no / bf16 / fp8 bias
+    (E4M3 / E5M2 codes with a power-of-two bias scale).  Small-integer data and
+    power-of-two scales: codes, amax, scale_inv and ring words bit-exact."""
+    c = mm_case(1000 + i)
+    r = synth.rng(9300, i)
+    fmt_c = [O.E4M3, O.E5M2][int(r.integers(0, 2))]
+    bias_kind = [None, "bf16", O.E4M3, O.E5M2][int(r.integers(0, 4))]
+    use_ring = bool(r.integers(0, 2))
+    M, N, K, batch = c["M"], c["N"], c["K"], c["batch"]
+    ba = 1 if c["bcast"] == "a" else batch
+    bb = 1 if c["bcast"] == "b" else batch
+    a = make_int_codes((ba, M, K), c["fa"], 9301, i)
+    b = make_int_codes((bb, N, K), c["fb"], 9302, i)
+    sa, sb = 2.0 ** c["sa_log2"], 2.0 ** c["sb_log2"]
+    bias_v = bias_t = bias_fmt = bias_scale = None
+    if bias_kind == "bf16":
+        bias_v = r.integers(-8, 9, size=N).astype(np.float64)
+        bias_t = torch.from_numpy(bias_v).to(torch.bfloat16).to(DEV)
+    elif bias_kind is not None:
+        codes = make_int_codes((N,), bias_kind, 9303, i)
+        sbias = 2.0 ** int(r.integers(-2, 3))
+        bias_v = O.dequant_bias(codes, bias_kind, sbias).astype(np.float64)
+        bias_t, bias_fmt, bias_scale = torch.from_numpy(codes).to(DEV), FID[bias_kind], scalar(sbias)
+    # output scale near fmt_max / (a typical |y|) so codes spread over the range
+    s_c = np.float32(O.FMT_MAX[fmt_c] / 2.0 ** int(r.integers(6, 14)))
+    ring = scale_t = None
+    if use_ring:
+        ring0 = O.Ring.new(4, 1.0)
+        ring0.hist[:] = r.uniform(0, 4000, size=4).astype(np.float32)
+        ring0.idx, ring0.scale = int(r.integers(0, 4)), s_c
+        ref = O.mm_quantized(a if batch > 1 else a[0], c["fa"], b if batch > 1 else b[0], c["fb"], fmt_c, sa, sb,
+                             bias_v, ring=ring0)
+        ring = ring_from_oracle(ring0)
+    else:
+        ref = O.mm_quantized(a if batch > 1 else a[0], c["fa"], b if batch > 1 else b[0], c["fb"], fmt_c, sa, sb,
+                             bias_v, scale=s_c)
+        scale_t = scalar(s_c)
+    sinv, amax = scalar(-1), scalar(-1)
+    out = fp8mi.fp8_mm_ex(operand(a, False, c["pad_a"]) if batch > 1 else operand(a, False, c["pad_a"])[0],
+                          operand(b, False, c["pad_b"]) if batch > 1 else operand(b, False, c["pad_b"])[0],
+                          FID[c["fa"]], FID[c["fb"]], scalar(sa), scalar(sb), bias_t, bias_fmt, bias_scale,
+                          out_fmt=FID[fmt_c], out_scale=scale_t, out_ring=ring, out_scale_inv=sinv, out_amax=amax)
+    torch.cuda.synchronize()
+    want = ref["codes"].reshape(out.shape)
+    assert np.array_equal(out.cpu().numpy(), want), c
+    assert f32_bits(amax) == as_bits(ref["amax"]), c
+    assert f32_bits(sinv) == as_bits(ref["scale_inv"]), c
+    if ring is not None:
+        assert np.array_equal(ring_state_words(ring), ref["ring"].words()), c
