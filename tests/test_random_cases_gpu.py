@@ -19,6 +19,8 @@ not list still meet the bar.
 * quantizing epilogue (60 cases): NT operands as above, E4M3 / E5M2 output
   codes with an explicit scale or a ring, no / bf16 / fp8-stored bias; codes,
   amax, scale_inv and ring words bit-exact.
+* bias gradient (60 cases), standalone or fused into the dual quantize, on
+  random shapes, offsets and paddings with exactly summable data: bit-exact.
 """
 import numpy as np
 import pytest
@@ -204,3 +206,36 @@ def test_random_gemm_fp8_out(i):
     assert f32_bits(sinv) == as_bits(ref["scale_inv"]), c
     if ring is not None:
         assert np.array_equal(ring_state_words(ring), ref["ring"].words()), c
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_random_bias_grad(i):
+    """The bias gradient, standalone and fused into the dual quantize, on
+    random shapes (rows, cols in [1, 1500]), bf16 / fp16 gradients at a base
+    0-7 elements past an allocation start with 0-40 elements of row padding.
+    Values are small integers times 2^-6, so every float64 sum is exact and
+    the once-rounded bf16 result must equal the oracle's bit for bit; the
+    fused call's codes, amax and scale_inv are bit-exact too."""
+    r = synth.rng(9400, i)
+    rows, cols = int(r.integers(1, 1501)), int(r.integers(1, 1501))
+    dt = ["bf16", "f16"][int(r.integers(0, 2))]
+    fused = bool(r.integers(0, 2))
+    v = (r.integers(-64, 65, size=(rows, cols)) * 2.0 ** -6).astype(np.float32)
+    dy = synth.f32_to_bf16_bits(v) if dt == "bf16" else v.astype(np.float16)
+    dyd = to_device(dy, dt, int(r.integers(0, 8)), cols + int(r.integers(0, 41)))
+    ref_db, _ = O.grad_bias(dy, dt)
+    if fused:
+        fmt = [O.E4M3, O.E5M2][int(r.integers(0, 2))]
+        s = np.float32(2.0 ** int(r.integers(-2, 6)))
+        ref = O.quantize(dy, dt, fmt, scale=s)
+        sinv, amax = scalar(-1), scalar(-1)
+        q, qt, db = fp8mi.fp8_quantize_dual_bias_grad(dyd, FID[fmt], scale=scalar(s), scale_inv_out=sinv,
+                                                      amax_out=amax)
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), ref["codes"]) and np.array_equal(qt.cpu().numpy(), ref["codes_t"])
+        assert f32_bits(amax) == as_bits(ref["amax"]) and f32_bits(sinv) == as_bits(ref["scale_inv"])
+    else:
+        db = fp8mi.fp8_bias_grad(dyd)
+        torch.cuda.synchronize()
+    got = db.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref_db), (rows, cols, dt, fused)
