@@ -42,6 +42,30 @@ def test_every_declared_symbol_is_exported(L):
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
 
 
+def _ctype(decl: str):
+    """ctypes type of one C parameter / return declaration of the header."""
+    decl = " ".join(decl.replace("const ", "").split())
+    if "*" in decl:
+        return C.c_char_p if decl.startswith("char") else C.c_void_p
+    base = decl.split()[0]
+    return {"int": C.c_int, "int32_t": C.c_int32, "int64_t": C.c_int64, "size_t": C.c_size_t,
+            "fp8mi_status": C.c_int}[base]
+
+
+def test_binding_signatures_match_the_header():
+    """Every declaration's return type and parameter types equal the ctypes
+    signature the binding installs (a mismatch would pass arguments in the
+    wrong registers or widths without any error)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = re.findall(r"FP8MI_API\s+([\w\s\*]+?)\b(\w+)\s*\(([^)]*)\)", text)
+    assert len(decls) == len(_lib.SIGNATURES)
+    for ret, name, params in decls:
+        res, args = _lib.SIGNATURES[name]
+        assert _ctype(ret) == res, name
+        plist = [p.strip() for p in params.split(",") if p.strip() and p.strip() != "void"]
+        assert [_ctype(p) for p in plist] == list(args), name
+
+
 def test_version_and_status_strings(L):
     assert L.fp8mi_version().decode().startswith("fp8mi")
     for s in range(8):
