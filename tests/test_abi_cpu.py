@@ -66,6 +66,28 @@ def test_binding_signatures_match_the_header():
         assert [_ctype(p) for p in plist] == list(args), name
 
 
+def test_error_text_is_per_thread(L):
+    """fp8mi_last_error is thread-local: rejected calls in four threads each
+    see their own text, and the calling thread sees none of them."""
+    import threading
+    texts = {}
+
+    def worker(t):
+        st = L.fp8_quantize(FAKE, 2, 4, 4, 4, 7 + t, 0, FAKE, 4, FAKE, None, 0, None, None, None)
+        texts[t] = (st, L.fp8mi_last_error().decode())
+
+    ths = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join(timeout=30)
+    for t in range(4):
+        st, text = texts[t]
+        assert st == ENUM and f"fmt {7 + t} " in text, (t, text)
+    main = L.fp8mi_last_error().decode()
+    assert all(f"fmt {7 + t} " not in main for t in range(4))
+
+
 def test_version_and_status_strings(L):
     assert L.fp8mi_version().decode().startswith("fp8mi")
     for s in range(8):
