@@ -96,16 +96,41 @@ def cpu_baseline(seconds_target=8.0):
 HOST_ONLY_SOURCES = ("abi.hip",)
 
 
+def code_tokens(src: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed, so
+    that edits to comments or layout do not count as kernel changes."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == '"' or c == "'":                      # string / char literal, kept verbatim
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
-    """sha256 of the HIP sources that hold or feed the kernels: counters
-    taken on other kernel sources are stale."""
+    """sha256 of the code (comments and layout ignored) of the HIP sources
+    that hold or feed the kernels: counters taken on other code are stale."""
     import hashlib
     csrc = os.path.join(ROOT, "fp8_tensor_scaled_quantize_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h")) and name not in HOST_ONLY_SOURCES:
             h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+            h.update(code_tokens(open(os.path.join(csrc, name)).read()).encode())
     return h.hexdigest()
 
 

@@ -1,8 +1,9 @@
 // Per-tensor-scaled fp8 GEMM on CDNA4 MFMA (gfx950), NT operands, fp32
 // accumulation, fused fp32 bias, one bf16 rounding of the output, batched
 // through grid.z with optional stride-0 broadcast.  The kernel template lives
-// in mm_fp8_kernel.h; this unit holds the bf16-output instantiations and the
-// dispatch, mm_fp8_q8.hip the fp8-output ones (the quantizing epilogue).
+// in mm_fp8_kernel.h; this unit holds the bf16-output NT instantiations, the
+// plain-load fallback and the dispatch, mm_fp8_q8.hip the fp8-output ones
+// (the quantizing epilogue) and mm_fp8_km.hip the K-major ones (layout tags).
 //
 // log:tests/extension -- the commit fusing the linear bias into the GEMM
 // epilogue (added in fp32 before the single bf16 rounding, guarded N tails,

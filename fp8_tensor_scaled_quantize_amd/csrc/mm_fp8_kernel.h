@@ -1,6 +1,6 @@
 // The per-tensor-scaled fp8 GEMM kernel template shared by the bf16-output
-// and the fp8-output (quantizing epilogue) translation units; see mm_fp8.hip
-// for the design.  Included by mm_fp8.hip and mm_fp8_q8.hip only.
+// (mm_fp8.hip), fp8-output (quantizing epilogue, mm_fp8_q8.hip) and K-major
+// (layout tags, mm_fp8_km.hip) translation units, which alone include it.
 #pragma once
 #include "fp8mi_device.h"
 #include "fp8mi_internal.h"
@@ -131,16 +131,18 @@ __device__ __forceinline__ v4f mfma_nt(const v8i& bfrag, const v8i& afrag, const
 }
 
 // ===========================================================================
-// Large-tile kernel: 256 x 256 block tile, 8 waves (2 along M x 4 along N),
-// each wave 128 x 64 = 8 x 4 MFMA tiles (128 fp32 accumulators per lane).
-// K advances 128 bytes per step through two LDS stages (2 x 64 KiB).  The
-// operands go from HBM/L2 straight into LDS (buffer_load_dwordx4 ... lds):
-// each load instruction fills 1 KiB = 8 tile rows, lane l writing 16 bytes at
-// l * 16, so lane l fetches the 16-byte chunk that the XOR swizzle places
-// there (row r0 + l/8, chunk (l%8) ^ (l/8)).  The loads of step k+1 are in
-// flight while step k's MFMAs run; one wait + barrier per step.  Rows past
-// the matrix edge and chunks past K read as zero: their buffer offsets lie
-// beyond the resource's byte count.
+// LDS-DMA kernel template (mm_fp8_dma).  The 256 x 256 headline tile: 8 waves
+// (2 along M x 4 along N), each wave 128 x 64 = 8 x 4 MFMA tiles (128 fp32
+// accumulators per lane); K advances 128 bytes per step through two LDS
+// stages (2 x 64 KiB).  The same template gives 256 x 192, 128 x 128 and,
+// with three stages, 64 x 128 and 64 x 64.  The operands go from HBM/L2
+// straight into LDS (buffer_load_dwordx4 ... lds): each load instruction
+// fills 1 KiB = 8 tile rows, lane l writing 16 bytes at l * 16, so lane l
+// fetches the 16-byte chunk that the XOR swizzle places there (row r0 + l/8,
+// chunk (l%8) ^ swz(l/8)).  The loads of the next step(s) are in flight while
+// this step's MFMAs run; one wait + barrier per step.  Rows past the matrix
+// edge and chunks past K read as zero: their buffer offsets lie beyond the
+// resource's byte count.
 // Workgroups are renumbered so that the ones a single XCD runs (the hardware
 // deals workgroup ids round-robin over the 8 XCDs) cover a compact block of
 // tiles -- group_m tile rows by consecutive tile columns -- and share their
