@@ -13,17 +13,24 @@
 // MI355X shape of the kernels (not the pages' sm_89 one):
 //  * quantize_flat: contiguous row layout; each wave moves 64 x 16-byte loads
 //    per step (one contiguous 1 KiB segment per load instruction) and writes
-//    one contiguous segment of codes per store instruction.  Persistent
-//    workgroups, the next group of steps loading while one is encoded.
-//  * quantize_tiled: 128-row x 64-column tiles, 256 threads.  Each thread
-//    loads a 4-row x 8-column micro block (16-byte loads, realigned in
-//    registers when a row segment does not start on 16 bytes), so
-//    the row-layout codes leave straight from registers and the transposed
-//    codes need only a 4x4 byte transpose in registers plus one 8 KiB LDS
-//    pass, after which every lane stores 16 contiguous bytes of a transposed
-//    row (128-byte segments per 8 lanes).  Persistent workgroups, the next
-//    tile loading while one is encoded.
-//  * amax: wave shuffle reduction, one device-scope atomic max per workgroup.
+//    one contiguous segment of codes per store instruction.  One-shot
+//    workgroups while the tensor fits 8 per CU, else persistent ones with the
+//    next group of steps loading while one is encoded.
+//  * quantize_tiled / quantize_tiled_pf: 128-row x 64-column tiles, 256
+//    threads.  Each thread loads a 4-row x 8-column micro block (16-byte
+//    loads, realigned in registers when a row segment does not start on 16
+//    bytes), so the row-layout codes leave straight from registers and the
+//    transposed codes need only a 4x4 byte transpose in registers plus one
+//    8 KiB LDS pass, after which every lane stores 16 contiguous bytes of a
+//    transposed row (128-byte segments per 8 lanes).  One tile per workgroup
+//    (quantize_tiled) or persistent workgroups with the next tile loading
+//    while one is encoded (quantize_tiled_pf), by the same size rule.
+//  * amax: wave and workgroup max on the raw bit patterns, then the ring's
+//    slot protocol (the last workgroup folds) or one device-scope atomic max
+//    into the caller's word.
+//  * current scaling: amax_partials writes one partial max per workgroup to
+//    the caller's workspace; the kernels above, instantiated with DYN, read
+//    them all and derive the scale in every wave (no atomics).
 #include "fp8mi_device.h"
 #include "fp8mi_internal.h"
 
