@@ -24,13 +24,6 @@ hipError_t launch_quantize_dynamic(const void* x, int dt, int64_t rows, int64_t 
                                    int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
                                    float* scale_inv_out, float* amax_out, uint32_t* parts, hipStream_t st);
 
-// Current scaling: amax partials into `parts` (dynamic_workspace_bytes()
-// bytes), then the quantize with s = fmt_max / amax.  Arguments validated.
-int64_t dynamic_workspace_bytes();
-hipError_t launch_quantize_dynamic(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
-                                   int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
-                                   float* scale_inv_out, float* amax_out, uint32_t* parts, hipStream_t st);
-
 hipError_t launch_amax_fold(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st);
 
 struct MmArgs {

@@ -912,8 +912,6 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, in
   return fmt == kE4M3 ? launch_fmt<kE4M3, false>(p, dt, mode, st) : launch_fmt<kE5M2, false>(p, dt, mode, st);
 }
 
-int64_t dynamic_workspace_bytes() { return (int64_t)kDynSlots * 4; }
-
 // Current scaling: the partials pass, then the ordinary quantize kernels with
 // the scale measured from the partials.
 hipError_t launch_quantize_dynamic(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
