@@ -148,7 +148,6 @@ __device__ __forceinline__ v4f mfma_nt(const v8i& bfrag, const v8i& afrag, const
 // tiles -- group_m tile rows by consecutive tile columns -- and share their
 // A and B panels in that XCD's L2.
 // ===========================================================================
-constexpr int kBigThreads = 512;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef int v4i __attribute__((ext_vector_type(4)));
 
