@@ -284,6 +284,44 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
     }
   };
 
+  // Issue chunk c (of NCH) of one stage's loads: this wave's load
+  // instructions c * LPW / NCH .. (c + 1) * LPW / NCH - 1 (A's LA first,
+  // then B's LB).
+  constexpr int NCH = 4;
+  auto issue_chunk = [&](int stage, int k0, int c) {
+    const bool past = k0 + 16 * lc >= K;
+    const uint32_t as = smem_lds + stage * STAGE, bs = as + BM * kBK;
+#pragma unroll
+    for (int q = c * LPW / NCH; q < (c + 1) * LPW / NCH; ++q) {
+      if (q < LA) {
+        if constexpr (KMA) {
+          const int qq = (wid * LA + q) * 64 + lane;
+          const int kr = qq / CPR_A, pos = qq % CPR_A;
+          const int rot = ((kr & 7) + (((kr >> 5) & 1) << 3)) % CPR_A;
+          const uint32_t c2 = (uint32_t)((pos + CPR_A - rot) % CPR_A);
+          dma16(rsa, as + (wid * LA + q) * 1024, k0 + kr >= K ? ext_a : (int)((uint32_t)kr * lda + 16 * c2),
+                (int)((uint32_t)k0 * lda));
+        } else {
+          const int r0 = (wid * LA + q) * 8;
+          dma16(rsa, as + r0 * kBK, past ? ext_a : (int)(va + (uint32_t)r0 * lda), k0);
+        }
+      } else {
+        const int qb = q - LA;
+        if constexpr (KMB) {
+          const int qq = (wid * LB + qb) * 64 + lane;
+          const int kr = qq / CPR_B, pos = qq % CPR_B;
+          const int rot = ((kr & 7) + (((kr >> 5) & 1) << 3)) % CPR_B;
+          const uint32_t c2 = (uint32_t)((pos + CPR_B - rot) % CPR_B);
+          dma16(rsb, bs + (wid * LB + qb) * 1024, k0 + kr >= K ? ext_b : (int)((uint32_t)kr * ldb + 16 * c2),
+                (int)((uint32_t)k0 * ldb));
+        } else {
+          const int r0 = (wid * LB + qb) * 8;
+          dma16(rsb, bs + r0 * kBK, past ? ext_b : (int)(vb + (uint32_t)r0 * ldb), k0);
+        }
+      }
+    }
+  };
+
   v4f acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
@@ -292,6 +330,76 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 
   const int nk = (K + kBK - 1) / kBK;
   const int r16 = lane & 15, g = lane >> 4;
+  auto frag_a = [&](const uint8_t* As, int i) -> v8i {
+    return KMA ? lds_frag_km<BM>(As, wm * WM + 16 * i, lane) : lds_frag(As, wm * WM + 16 * i + r16, g);
+  };
+  auto frag_b = [&](const uint8_t* Bs, int j) -> v8i {
+    return KMB ? lds_frag_km<BN>(Bs, wn * WN + 16 * j, lane) : lds_frag(Bs, wn * WN + 16 * j + r16, g);
+  };
+  if constexpr (STAGES == 2) {
+    // Two stages, A fragments read two rows ahead.  Iteration kt enters with
+    // step kt's B fragments and A fragments 0 and 1 in registers (A rows
+    // rotate through four registers, ar[i % 4]) and half of step kt + 1's
+    // loads issued; the other half goes out after rows 0 and 1.  After row
+    // TI - 3 the wave waits for its reads of stage kt (the last A fragment
+    // was read two rows earlier) and its loads of step kt + 1, and passes the
+    // barrier: every wave is done with stage kt and step kt + 1 is visible.
+    // Rows TI - 2 and TI - 1 run after the barrier while step kt + 1's first
+    // two A fragments (into the registers rows TI - 4 and TI - 3 freed) and,
+    // as each MFMA of the last row issues, its B fragments are read; then the
+    // first half of step kt + 2's loads goes into stage kt, now free.  At the
+    // last step these reads fetch the idle stage and go unused.
+    static_assert(TI >= 4 && TI % 4 == 0, "two-stage schedule needs a multiple of four A rows per wave");
+    v8i bf[TJ], ar[4];
+    if (nk > 0) issue_all(0, 0);
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) bf[j] = frag_b(smem + BM * kBK, j);
+    ar[0] = frag_a(smem, 0);
+    ar[1] = frag_a(smem, 1);
+    if (nk > 1) {
+      issue_chunk(1, kBK, 0);
+      issue_chunk(1, kBK, 1);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint8_t* As = smem + (kt & 1) * STAGE;
+      const uint8_t* An = smem + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        if (i + 2 < TI) ar[(i + 2) & 3] = frag_a(As, i + 2);
+        if (i == TI - 2) {  // after the barrier: step kt + 1's first two A fragments
+          ar[(i + 2) & 3] = frag_a(An, 0);
+          ar[(i + 3) & 3] = frag_a(An, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          acc[i][j] = mfma_nt<FA, FB>(bf[j], ar[i & 3], acc[i][j]);
+          if (i == TI - 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            bf[j] = frag_b(An + BM * kBK, j);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 2 && kt + 1 < nk) issue_chunk((kt + 1) & 1, (kt + 1) * kBK, 2 + i);
+        if (i == TI - 3) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          wait_vmem();
+          __syncthreads();
+          if (kt + 2 < nk) {
+            issue_chunk(kt & 1, (kt + 2) * kBK, 0);
+            issue_chunk(kt & 1, (kt + 2) * kBK, 1);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // every wave passed the last barrier after its last read of a stage the
+    // epilogue overwrites: wait for the idle-stage reads of the last step too
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  } else {
   // prologue: steps 0 .. STAGES-2 in flight; wait for step 0 only
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -327,6 +435,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
       wait_vmem();
     }
     __syncthreads();
+  }
   }
 
   // Epilogue: y = acc * fl32(sa * sb) + bias[j] in fp32, then one bf16
