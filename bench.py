@@ -51,10 +51,11 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(seconds_target=8.0):
+def cpu_baseline(seconds_target=6.0):
     """The CPU oracle on a bounded sample of the same workload: the GEMM on a
-    block of output rows of the 4096^3 problem, and the dual-layout quantize
-    of a row block of the 8192x1536 tensor."""
+    block of output rows of the 4096^3 problem (up to the whole problem), and
+    the dual-layout quantize of the 8192x1536 tensor, each repeated until
+    about seconds_target of CPU time so the rate is stable."""
     import numpy as np
     import oracle as O
     import synth
@@ -79,16 +80,25 @@ def cpu_baseline(seconds_target=8.0):
         t0 = time.perf_counter()
         O.mm(a, O.E4M3, b, O.E4M3, 0.5, 0.25, bias)
         t1 = time.perf_counter()
-    mm_tflops = 2.0 * rows * N * K / (t1 - t0) / 1e12
+    mm_runs, mm_s = 1, t1 - t0
+    while mm_s < seconds_target:
+        t0 = time.perf_counter()
+        O.mm(a, O.E4M3, b, O.E4M3, 0.5, 0.25, bias)
+        mm_s += time.perf_counter() - t0
+        mm_runs += 1
+    mm_tflops = 2.0 * rows * N * K * mm_runs / mm_s / 1e12
     qrows = QSHAPE[0]
     x = synth.gaussian((qrows, QSHAPE[1]), 1.0, "bf16", 90, 4)
-    t2 = time.perf_counter()
-    O.quantize(x, "bf16", O.E4M3, ring=O.Ring.new(HIST, 1.0))
-    t3 = time.perf_counter()
-    q_gbs = qrows * QSHAPE[1] * (2 + 2) / (t3 - t2) / 1e9
+    q_runs, q_s = 0, 0.0
+    while q_s < seconds_target:
+        t2 = time.perf_counter()
+        O.quantize(x, "bf16", O.E4M3, ring=O.Ring.new(HIST, 1.0))
+        q_s += time.perf_counter() - t2
+        q_runs += 1
+    q_gbs = qrows * QSHAPE[1] * (2 + 2) * q_runs / q_s / 1e9
     return {"value": round(mm_tflops, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"GEMM: {rows} output rows of {M}x{N}x{K} (float64 BLAS + bf16 rounding, {t1 - t0:.2f} s); "
-                      f"quantize dual: {qrows}x{QSHAPE[1]} bf16 rows ({t3 - t2:.2f} s)",
+            "sample": f"GEMM: {rows} output rows of {M}x{N}x{K} (float64 BLAS + bf16 rounding), {mm_runs} runs, "
+                      f"{mm_s:.1f} s; quantize dual: {qrows}x{QSHAPE[1]} bf16, {q_runs} runs, {q_s:.1f} s",
             "quantize_GBps": round(q_gbs, 4), "host_cpus": len(os.sched_getaffinity(0))}
 
 
