@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -41,6 +42,14 @@ int device_cu_count() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+int env_int_in(const char* name, int lo, int hi, int dflt) {
+  const char* e = getenv(name);
+  if (!e || !*e) return dflt;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  return (*end == '\0' && v >= lo && v <= hi) ? (int)v : dflt;
 }
 
 static_assert(kDynWorkspaceBytes == FP8MI_DYNAMIC_WORKSPACE_BYTES, "dynamic workspace size");

@@ -8,6 +8,11 @@ namespace fp8mi {
 // Compute-unit count of the current device (cached per device).
 int device_cu_count();
 
+// Integer tuning override from the environment: the value of `name` when it
+// is a decimal integer in [lo, hi], else dflt (unset, malformed or out of
+// range values are ignored).
+int env_int_in(const char* name, int lo, int hi, int dflt);
+
 // mode: 0 row, 1 transposed, 2 dual.  Arguments already validated.  With
 // bias_ws (dual, bf16/fp16 input) the dual kernel also writes fp64 column sums
 // per 128-row tile to bias_ws[tile row][col] (the grad_bias workspace layout).

@@ -5,8 +5,6 @@
 #include "fp8mi_device.h"
 #include "fp8mi_internal.h"
 
-#include <cstdlib>
-
 namespace fp8mi {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -595,8 +593,8 @@ static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
 }
 
 static inline int pick_tile(const MmArgs& p, int ncu) {
-  static const int forced = [] { const char* e = getenv("FP8MI_MM_TILE"); return e ? atoi(e) : -1; }();
-  if (forced >= 0 && forced < 6 && forced != 4) return forced;
+  static const int forced = env_int_in("FP8MI_MM_TILE", 0, 5, -1);
+  if (forced >= 0 && forced != 4) return forced;
   const int64_t tm = (p.M + 255) / 256;
   const int64_t t256 = tm * ((p.N + 255) / 256) * p.batch, t192 = tm * ((p.N + 191) / 192) * p.batch;
   if (10 * (t256 > t192 ? t256 : t192) < 6 * (int64_t)ncu) {

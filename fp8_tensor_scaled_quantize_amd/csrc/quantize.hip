@@ -34,8 +34,6 @@
 #include "fp8mi_device.h"
 #include "fp8mi_internal.h"
 
-#include <cstdlib>
-
 namespace fp8mi {
 
 struct QuantArgs {
@@ -832,10 +830,6 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // persistent count for tuning.
 constexpr int kOneShotBlocksPerCU = 8;
 constexpr int kPersistBlocksPerCU = 3;
-static int env_int(const char* name, int dflt) {
-  const char* e = getenv(name);
-  return e ? atoi(e) : dflt;
-}
 
 template <int DT, int FMT, int M, bool BG, bool DYN>
 static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantArgs& p, int64_t tiles_c,
@@ -851,7 +845,7 @@ static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantAr
 template <int DT, int FMT, bool DYN>
 static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int ncu = device_cu_count();
-  static const int persist_bpc = env_int("FP8MI_Q_BPC", kPersistBlocksPerCU);
+  static const int persist_bpc = env_int_in("FP8MI_Q_BPC", 1, 16, kPersistBlocksPerCU);
   const int64_t n = p.rows * p.cols;
   const bool contiguous_row = mode == kRow && p.ld_x == p.cols && p.ld_row == p.cols &&
                               (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
@@ -918,7 +912,7 @@ hipError_t launch_quantize_dynamic(const void* x, int dt, int64_t rows, int64_t 
                                    int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
                                    float* scale_inv_out, float* amax_out, uint32_t* parts, hipStream_t st) {
   const int ncu = device_cu_count();
-  static const int amax_bpc = env_int("FP8MI_AMAX_BPC", kAmaxBlocksPerCU);
+  static const int amax_bpc = env_int_in("FP8MI_AMAX_BPC", 1, 16, kAmaxBlocksPerCU);
   const int eb = dt == kF32 ? 4 : 2;
   // as few load batches per thread as the cap allows, spread evenly (a
   // half-filled last batch would cost a whole extra round trip)
