@@ -576,10 +576,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 // the 8-wave big-tile kernels whenever their tiles (x batch) cover at least
 // 60% of the CUs -- one round of big tiles beats several rounds of small ones
 // even with part of the chip idle -- choosing 256 x 192 over 256 x 256 when it
-// needs less work per CU (rounds of workgroups x tile width: the backward
-// GEMMs of the 1536-wide linear get 256 and 216 workgroups instead of 192 and
-// 162, 10-11% faster), and the 64x128 / 4-wave kernel (two per CU, three LDS
-// stages) below 60% -- or 64x64 when the 64x128 tiles number at most one per CU.
+// needs less time per CU (the backward GEMMs of the 1536-wide linear get 256
+// and 216 workgroups instead of 192 and 162, 10-11% faster), and the 64x128 /
+// 4-wave kernel (two per CU, three LDS stages) below 60% -- or 64x64 when the
+// 64x128 tiles number at most one per CU.
 // 128x128 is reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128
 // kernel remains for operands whose byte extent does not fit a 32-bit buffer
 // offset.
@@ -604,8 +604,13 @@ static inline int pick_tile(const MmArgs& p, int ncu) {
     const int64_t t128 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
     return t128 <= (int64_t)ncu ? 5 : 2;
   }
-  // per-CU work of the big-tile family: rounds of workgroups x tile width
-  const int64_t cost256 = ((t256 + ncu - 1) / ncu) * 256, cost192 = ((t192 + ncu - 1) / ncu) * 192;
+  // per-CU time of the big-tile family: rounds of workgroups x the time of
+  // one round, a 256 x 192 round taking ~0.9 of a 256 x 256 one (measured
+  // per K step on MI355X; its MFMA work is 0.75 of it).  So 256 x 192 wins
+  // when it needs no more rounds (the backward GEMMs of the 1536-wide
+  // linear), 256 x 256 when it saves a round (8192 x 6912 x 1536: 4 rounds
+  // instead of 5, 3% faster).
+  const int64_t cost256 = ((t256 + ncu - 1) / ncu) * 256, cost192 = ((t192 + ncu - 1) / ncu) * 230;
   return cost192 < cost256 ? 3 : 0;
 }
 
