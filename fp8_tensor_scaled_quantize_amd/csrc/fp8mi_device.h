@@ -149,21 +149,29 @@ template <int FMT> __device__ __forceinline__ float scale_from_max(float m) {
 }
 
 // ---------------------------------------------------------------------------
-// Ring fold, executed by one full wave (64 lanes): write amax into
-// hist[slot], advance the slot modulo H, publish fmt_max / max(hist) (1.0
-// when that maximum is 0 or not finite, or the quotient is not a finite
-// positive number).  The lanes read the history in parallel; the maximum of
-// the new window is max(amax, hist[i] for i != slot), which is exact in any
-// order.
+// Ring fold, executed by one full wave (64 lanes): amax = v (REDUCE false,
+// the same value in every lane) or the maximum of the lanes' v (REDUCE
+// true); write amax into hist[slot], advance the slot modulo H,
+// publish fmt_max / max(hist) (1.0 when that maximum is 0 or not finite, or
+// the quotient is not a finite positive number).  The slot index and the
+// first 64 history entries are loaded before anything waits, so they travel
+// together with whatever loads the caller left in flight for v (one memory
+// round trip instead of two or three).  The maximum of the new window
+// is max(amax, hist[i] for i != slot), which is exact in any order.
 // ---------------------------------------------------------------------------
-template <int FMT>
-__device__ void ring_fold_wave(uint32_t* ring, int H, float amax, float* scale_inv_out, float s_used,
-                               float* amax_out) {
+template <int FMT, bool REDUCE = false>
+__device__ void ring_fold_wave(uint32_t* ring, int H, float v, float* scale_inv_out, float s_used, float* amax_out) {
   const int lane = threadIdx.x & 63;
   const float* hist = reinterpret_cast<const float*>(ring);
-  const uint32_t slot = ring[H + 1] % (uint32_t)H;
+  // unconditional loads (lanes at or past H re-read entry 0, unused), so no
+  // branch separates them and neither waits for the other
+  const float h0 = hist[lane < H ? lane : 0];
+  const uint32_t slot_word = ring[H + 1];
+  const float amax = REDUCE ? wave_max(v) : v;
+  const uint32_t slot = slot_word % (uint32_t)H;
   float m = amax;
-  for (int i = lane; i < H; i += 64)
+  if (lane < H && (uint32_t)lane != slot) m = fmaxf(m, h0);
+  for (int i = lane + 64; i < H; i += 64)
     if ((uint32_t)i != slot) m = fmaxf(m, hist[i]);
   m = wave_max(m);
   if (lane == 0) {
@@ -252,9 +260,9 @@ __device__ void ring_block_done(uint32_t* ring, int H, float block_amax, float s
   if (*flag == 0u || threadIdx.x >= 64) return;
   // The last workgroup: wave 0 reduces the slots, folds, clears the scratch.
   const int lane = threadIdx.x;
-  float a = (uint32_t)lane < nslot ? __uint_as_float(dev_load(scratch + lane * kFoldSlotStride)) : 0.0f;
-  a = wave_max(a);
-  ring_fold_wave<FMT>(ring, H, a, scale_inv_out, s_used, amax_out);
+  // the slot reads stay in flight while the fold issues its history loads
+  const float a = (uint32_t)lane < nslot ? __uint_as_float(dev_load(scratch + lane * kFoldSlotStride)) : 0.0f;
+  ring_fold_wave<FMT, true>(ring, H, a, scale_inv_out, s_used, amax_out);
   if ((uint32_t)lane < nslot) {
     (void)dev_xchg(scratch + lane * kFoldSlotStride, 0u);
     (void)dev_xchg(scratch + lane * kFoldSlotStride + 1, 0u);
