@@ -106,9 +106,13 @@ template <int FMT> __device__ __forceinline__ uint32_t enc4_exact(float a, float
 // bf16 round to nearest even from fp32 (overflow to inf, NaN kept quiet).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  // both results, then a select: written with an early return for NaN, the
+  // compiler emitted an exec-mask branch per value, which made the GEMM's
+  // 128-value-per-lane epilogue take ~5 µs
   const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = ((u >> 16) | 0x40u) & 0xFFFFu;
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? quiet_nan : rounded;
 }
 
 // ---------------------------------------------------------------------------
