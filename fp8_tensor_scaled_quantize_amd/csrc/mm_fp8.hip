@@ -115,15 +115,17 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
     for (int j = 0; j < TJ; ++j) {
       const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng;
       if (gn >= p.N) continue;
-      uint32_t h[4];
+      float y[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float bv = (p.bias && gn + r < p.N) ? load_bias(p, gn + r, bscale) : 0.0f;
-        h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bv));
+        y[r] = fmaf(acc[i][j][r], sab, bv);
       }
+      const uint2 w = bf16x4_rne(y[0], y[1], y[2], y[3]);
+      const uint32_t h[4] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16};
       uint16_t* dst = C + gm * p.ldc + gn;
       if (gn + 4 <= p.N && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *reinterpret_cast<uint2*>(dst) = w;
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)

@@ -556,11 +556,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
       const int lm = wm * WM + 16 * i + r16;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bias_v[j][r]));
         *reinterpret_cast<uint2*>(Cs + lm * CROW + wn * WN + 16 * j + 4 * ng) =
-            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            bf16x4_rne(fmaf(acc[i][j][0], sab, bias_v[j][0]), fmaf(acc[i][j][1], sab, bias_v[j][1]),
+                       fmaf(acc[i][j][2], sab, bias_v[j][2]), fmaf(acc[i][j][3], sab, bias_v[j][3]));
       }
     }
     __syncthreads();
@@ -583,13 +581,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
     for (int j = 0; j < TJ; ++j) {
       const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng;
       if (gn >= p.N) continue;
-      uint32_t h[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(fmaf(acc[i][j][r], sab, bias_v[j][r]));
+      const uint2 w = bf16x4_rne(fmaf(acc[i][j][0], sab, bias_v[j][0]), fmaf(acc[i][j][1], sab, bias_v[j][1]),
+                                 fmaf(acc[i][j][2], sab, bias_v[j][2]), fmaf(acc[i][j][3], sab, bias_v[j][3]));
       uint16_t* dst = C + gm * p.ldc + gn;
       if (gn + 4 <= p.N && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *reinterpret_cast<uint2*>(dst) = w;
       } else {
+        const uint32_t h[4] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16};
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (gn + r < p.N) dst[r] = (uint16_t)h[r];
