@@ -566,7 +566,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
     // past RPW * LPR idle when BN / 8 does not divide 64, e.g. BN = 192)
     constexpr int LPR = BN / 8, RPW = 64 / LPR;
     const int sub = lane / LPR, cl = lane % LPR;
-#pragma unroll 4
+    // fully unrolled: every LDS row read is in flight before the first store
+    // (by four: 1-2.6% slower on 4096^3 and the linear's GEMMs)
+#pragma unroll
     for (int rr = wid * RPW + sub; sub < RPW && rr < BM; rr += RPW * NWAVES) {
       const uint4 v = *reinterpret_cast<const uint4*>(Cs + rr * CROW + 8 * cl);
       *reinterpret_cast<uint4*>(C + (m0 + rr) * p.ldc + n0 + 8 * cl) = v;
