@@ -283,8 +283,10 @@ fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_
     if ((stride_a % 16) || (stride_b % 16))
       return fail(FP8MI_ERR_UNSUPPORTED, "batch strides of a and b must be multiples of 16");
   }
-  // the smallest tile is 64 x 64: its count bounds every kernel's grid
-  if ((M + 63) / 64 > 65535 || batch > 65535 || (N + 63) / 64 > 0x7FFFFFFF / ((M + 63) / 64))
+  // the smallest tile is 64 x 64: its count bounds every kernel's grid; below
+  // 2^29 per batch, the kernels' tile arithmetic fits 32 bits (no allocation
+  // of one GPU comes near: 2^29 such tiles are 4 TB of bf16 output)
+  if ((M + 63) / 64 > 65535 || batch > 65535 || (N + 63) / 64 > 0x1FFFFFFF / ((M + 63) / 64))
     return fail(FP8MI_ERR_UNSUPPORTED, "M=%lld N=%lld batch=%lld beyond the launch grid", (long long)M, (long long)N,
                 (long long)batch);
   p.a = a; p.b = b; p.lda = lda; p.ldb = ldb; p.stride_a = stride_a; p.stride_b = stride_b;

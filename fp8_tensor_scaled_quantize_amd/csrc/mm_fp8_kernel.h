@@ -192,17 +192,20 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voff, int soff
       : "memory");
 }
 
-__device__ __forceinline__ void tile_coords(int64_t wg, int64_t tiles_m, int64_t tiles_n, int group_m,
+// 32-bit arithmetic: the launch checks keep the tile count of a batch below
+// 2^31, and 64-bit divisions cost a few hundred instructions per workgroup.
+__device__ __forceinline__ void tile_coords(int64_t wg64, int64_t tiles_m64, int64_t tiles_n64, int group_m,
                                             int64_t& tm, int64_t& tn) {
-  const int64_t T = tiles_m * tiles_n;
-  const int64_t full = (T / 8) * 8;
-  int64_t id = wg;
-  if (wg < full) id = (wg % 8) * (full / 8) + wg / 8;  // same-XCD workgroups get consecutive ids
-  const int64_t per_group = (int64_t)group_m * tiles_n;
-  const int64_t g = id / per_group, r = id % per_group;
-  const int64_t rows_here = (tiles_m - g * group_m) < group_m ? (tiles_m - g * group_m) : group_m;
-  tm = g * group_m + r % rows_here;
-  tn = r / rows_here;
+  const uint32_t wg = (uint32_t)wg64, tiles_m = (uint32_t)tiles_m64, tiles_n = (uint32_t)tiles_n64;
+  const uint32_t gm = (uint32_t)group_m;
+  const uint32_t full = (tiles_m * tiles_n / 8u) * 8u;
+  uint32_t id = wg;
+  if (wg < full) id = (wg % 8u) * (full / 8u) + wg / 8u;  // same-XCD workgroups get consecutive ids
+  const uint32_t per_group = gm * tiles_n;
+  const uint32_t g = id / per_group, r = id % per_group;
+  const uint32_t rows_here = (tiles_m - g * gm) < gm ? (tiles_m - g * gm) : gm;
+  tm = (int64_t)(g * gm + r % rows_here);
+  tn = (int64_t)(r / rows_here);
 }
 
 // LAY: bit 0 -- A given K-major ([K, M], lda >= M), bit 1 -- B given K-major

@@ -193,7 +193,7 @@ FP8MI_API fp8mi_status fp8_amax_fold(uint32_t* ring, int32_t hist_len, const flo
  * FP8MI_ERR_UNSUPPORTED); lda, ldb >= K; ldc >= N; c 2-byte aligned; with
  * batch > 1, stride_c >= M * ldc.  M, N or batch 0: no-op.  K == 0 writes
  * bf16(bias) (or zeros).  Launch-grid limits: ceil(M / 64) <= 65535,
- * batch <= 65535 and ceil(M / 64) * ceil(N / 64) < 2^31 (else
+ * batch <= 65535 and ceil(M / 64) * ceil(N / 64) < 2^29 (else
  * FP8MI_ERR_UNSUPPORTED).
  */
 FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_a,

@@ -326,6 +326,7 @@ def test_mm_ex_rejects(L):
     assert call(batch=4, sa=big) == SHAPE             # batch x stride_a
     assert call(lay=1, M=64, lda=big - big % 16) == SHAPE   # K-major A: K x lda
     assert call(M=1 << 20, N=1 << 24, ldc=1 << 24) == UNSUP  # 2^32 tiles of 64 x 64
+    assert call(M=1 << 16, N=1 << 25, ldc=1 << 25) == UNSUP  # 2^29 tiles of 64 x 64
     # the plain fp8_mm refuses an fp8 bias type (it has no bias scale)
     assert L.fp8_mm(FAKE, 0, 32, 0, FAKE, 0, 32, 0, 4, 4, 32, 1, None, None, FAKE, 3, FAKE, 4, 16, None) == ENUM
 
