@@ -102,6 +102,15 @@ template <int FMT> __device__ __forceinline__ uint32_t enc4_exact(float a, float
   return enc_exact<FMT>(a) | (enc_exact<FMT>(b) << 8) | (enc_exact<FMT>(c) << 16) | (enc_exact<FMT>(d) << 24);
 }
 
+// A scale s for which x * s is NaN only where x is NaN: finite and nonzero.
+// With any other scale (0, +-inf, NaN) 0 * inf or inf * 0 makes a NaN out of
+// a non-NaN input, so the kernels send every element to enc_exact, which
+// encodes the product itself; the NaN test on the raw input that picks the
+// fast conversion is valid only for a regular scale.
+__device__ __forceinline__ bool scale_regular(float s) {
+  return s != 0.0f && __builtin_fabsf(s) <= 3.40282347e38f;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 round to nearest even from fp32 (overflow to inf, NaN kept quiet).
 // ---------------------------------------------------------------------------

@@ -68,6 +68,11 @@ hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 hipError_t launch_mm_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 // bf16-output GEMM with K-major operand(s) (p.layout != 0, extents below 2^31 bytes).
 hipError_t launch_mm_km(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+// Short K (K <= kPreciseMaxK, mm_fp8_kernel.h): the precise-accumulation
+// kernels, bf16 NT / bf16 K-major / fp8 output (operand extents below 2^31 bytes).
+hipError_t launch_mm_prec_nt(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+hipError_t launch_mm_prec_km(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+hipError_t launch_mm_prec_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 // One fp32 word set to 0 on the stream (a fill kernel, capturable).
 hipError_t launch_zero_word(float* p, hipStream_t st);
 

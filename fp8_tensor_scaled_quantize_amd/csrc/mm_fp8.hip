@@ -24,7 +24,7 @@
 
 namespace fp8mi {
 
-template <int BM, int BN, int FA, int FB>
+template <int BM, int BN, int FA, int FB, bool PREC>
 __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;             // 2 x 2 waves
   constexpr int TI = WM / 16, TJ = WN / 16;           // MFMA tiles per wave
@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_nt<FA, FB>(bfr[j], af[i], acc[i][j]);
+      for (int j = 0; j < TJ; ++j) acc[i][j] = mma<FA, FB, PREC>(bfr[j], af[i], acc[i][j]);
     __syncthreads();
     if (kt + 1 < nk) {
       sstore();
@@ -137,11 +137,15 @@ __global__ void __launch_bounds__(kMmThreads) mm_fp8_tile(MmArgs p) {
 
 // Large operands (byte extents beyond a 32-bit buffer offset) take the
 // 128x128 plain-load kernel; everything else the LDS-DMA big-tile family.
+// Short K takes the precise accumulation in either case.
 template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStream_t st) {
-  if (mm_fits31(p)) return launch_dma_family<FA, FB, -1>(p, st);
+  if (mm_fits31(p)) return mm_precise(p) ? launch_mm_prec_nt(p, FA, FB, st) : launch_dma_family<FA, FB, -1>(p, st);
   constexpr int BM = 128, BN = 128;
   const dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM), (unsigned)p.batch);
-  hipLaunchKernelGGL((mm_fp8_tile<BM, BN, FA, FB>), grid, dim3(kMmThreads), 0, st, p);
+  if (mm_precise(p))
+    hipLaunchKernelGGL((mm_fp8_tile<BM, BN, FA, FB, true>), grid, dim3(kMmThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((mm_fp8_tile<BM, BN, FA, FB, false>), grid, dim3(kMmThreads), 0, st, p);
   return hipGetLastError();
 }
 

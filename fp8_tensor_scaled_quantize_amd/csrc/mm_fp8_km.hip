@@ -4,29 +4,21 @@
 // transposed operands into the GEMM).  The mm_fp8_dma kernels load such a
 // tile into LDS as k-rows (LDS-DMA, swizzled 16-byte chunks) and build the
 // MFMA operand fragments with gfx950's LDS transpose read (ds_read_b64_tr_b8).
-// bf16 output; the same tile family and dispatch as the NT GEMM.
+// bf16 output; the same tile family and dispatch as the NT GEMM (64 x 64 included).
 #include "mm_fp8_kernel.h"
 
 namespace fp8mi {
 
-template <int FA, int FB, int LAY> static hipError_t launch_km_lay(const MmArgs& p, hipStream_t st) {
-  switch (pick_tile(p, device_cu_count())) {
-    case 0: return launch_dma<FA, FB, 256, 256, 2, 4, 1, -1, LAY>(p, st);
-    case 3: return launch_dma<FA, FB, 256, 192, 2, 4, 1, -1, LAY>(p, st);
-    case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2, -1, LAY>(p, st);
-    default: return launch_dma<FA, FB, 64, 128, 1, 4, 2, -1, LAY>(p, st);
-  }
-}
-
 template <int FA, int FB> static hipError_t launch_km_fmts(const MmArgs& p, hipStream_t st) {
   switch (p.layout) {
-    case 1: return launch_km_lay<FA, FB, 1>(p, st);
-    case 2: return launch_km_lay<FA, FB, 2>(p, st);
-    default: return launch_km_lay<FA, FB, 3>(p, st);
+    case 1: return launch_dma_family<FA, FB, -1, 1>(p, st);
+    case 2: return launch_dma_family<FA, FB, -1, 2>(p, st);
+    default: return launch_dma_family<FA, FB, -1, 3>(p, st);
   }
 }
 
 hipError_t launch_mm_km(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st) {
+  if (mm_precise(p)) return launch_mm_prec_km(p, fmt_a, fmt_b, st);
   if (fmt_a == kE4M3 && fmt_b == kE4M3) return launch_km_fmts<kE4M3, kE4M3>(p, st);
   if (fmt_a == kE5M2 && fmt_b == kE4M3) return launch_km_fmts<kE5M2, kE4M3>(p, st);
   if (fmt_a == kE4M3 && fmt_b == kE5M2) return launch_km_fmts<kE4M3, kE5M2>(p, st);

@@ -205,7 +205,8 @@ constexpr int kFlatUnroll = 2;                                          // block
 
 // Encode one lane's 16 elements of a wave step (already loaded) and store the codes.
 template <int DT, int FMT, int NL, int EPL>
-__device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t* out_w0, int lane, float s) {
+__device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t* out_w0, int lane, float s,
+                                                   bool sreg) {
   float f[kFlatElemsPerThread];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
@@ -224,7 +225,7 @@ __device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t
   const bool nan = am.has_nan();
   const float camax = nan ? nan_free_absmax<kFlatElemsPerThread>(f) : am.value();
   uint32_t code[kFlatElemsPerThread / 4];
-  if (!nan) {
+  if (!nan && sreg) {
 #pragma unroll
     for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
       code[q] = cvt4<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
@@ -277,11 +278,12 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
   if (ng > 0) load_group(va, first);
   // the scale is read after the first loads are out (it does not gate them)
   const float s = read_scale<FMT, DYN>(p);
+  const bool sreg = scale_regular(s);
   auto encode_group = [&](const uint4 (&v)[U][NL], int64_t g0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t w0 = (g0 + u) * kFlatBlockStep + (int64_t)wid * kFlatWaveStep;
-      amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v[u], p.out_row + w0, lane, s));
+      amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v[u], p.out_row + w0, lane, s, sreg));
     }
   };
   int64_t g = 0;
@@ -308,7 +310,7 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
 #pragma unroll
       for (int j = 0; j < NL; ++j)
         v[j] = *reinterpret_cast<const uint4*>(xb + (w0 + (int64_t)(j * 64 + lane) * EPL) * EB);
-      amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v, p.out_row + w0, lane, s));
+      amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v, p.out_row + w0, lane, s, sreg));
     } else if (w0 < n) {
       // ragged end of the tensor: element by element, same lane mapping
 #pragma unroll
@@ -351,6 +353,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
   __shared__ double bg_red[BG ? kTileThreads / 64 : 1][BG ? kTileC : 1];
   constexpr int EB = In<DT>::kBytes;
   const float s = read_scale<FMT, DYN>(p);
+  const bool sreg = scale_regular(s);
   const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
   float amax = 0.0f;
   const char* xb = static_cast<const char*>(p.x);
@@ -408,7 +411,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
     }
     amax = fmaxf(amax, camax);
     uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
-    if (!nan) {
+    if (!nan && sreg) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -540,7 +543,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
     }
   };
 
-  auto process_tile = [&](int64_t tile, const TileRaw<DT>& L, float s) {
+  auto process_tile = [&](int64_t tile, const TileRaw<DT>& L, float s, bool sreg) {
     const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
     const int64_t cc = c0 + 8 * cg;  // this thread's first column
     float f[4][8];
@@ -585,7 +588,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
     }
     amax = fmaxf(amax, camax);
     uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
-    if (!nan) {
+    if (!nan && sreg) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -683,9 +686,10 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
   TileRaw<DT> cur, nxt;
   if (t_first < t_last) load_tile(t_first, cur);
   const float s = read_scale<FMT, DYN>(p);  // after the first loads are out
+  const bool sreg = scale_regular(s);
   for (int64_t tile = t_first; tile < t_last; ++tile) {
     if (tile + 1 < t_last) load_tile(tile + 1, nxt);
-    process_tile(tile, cur, s);
+    process_tile(tile, cur, s, sreg);
     cur = nxt;
   }
   quant_block_done<FMT, kTileThreads, DYN>(p, amax, s, red);

@@ -3,7 +3,8 @@ epilogue -- against the oracle's mm_quantized / dequant_bias.
 
 The pre-quantization output y is fp32 on the device and exact (float64) in
 the oracle, so the GEMM tolerance of test_mm_gpu carries over to y:
-    tol = 1e-5 * sum_k |a_ik b_jk| + the fp8-MFMA group-truncation term + 2^-22 |y|.
+    tol = 1e-5 * sum_k |a_ik b_jk| + 2^-22 |y|
+(the stated bound's sum term, plus the fp32 rounding of y itself).
 A code is accepted when it lies between the codes of (y - tol) and (y + tol)
 (quantization is monotone), at least 99.9 % of the codes must equal the
 oracle's exactly, amax must lie within the same band around max |y|, and the
@@ -17,7 +18,7 @@ import torch
 
 import oracle as O
 import synth
-from tests.gpu_util import DEV, as_bits, f32_bits, mfma_group_term, np_bf16_bits, ring_from_oracle, ring_state_words, scalar
+from tests.gpu_util import DEV, as_bits, f32_bits, np_bf16_bits, ring_from_oracle, ring_state_words, scalar
 from tests.test_mm_gpu import make_codes, make_int_codes, sample_rows, to_dev_codes
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +29,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def y_band(a, fa, b, fb, sa, sb, bias):
     y, mag = O.mm_exact_f64(a, fa, b, fb, sa, sb, bias)
-    tol = 1e-5 * mag + mfma_group_term(a, fa, b if b.ndim == 2 else b, fb, sa, sb) + 2.0 ** -22 * np.abs(y)
+    tol = 1e-5 * mag + 2.0 ** -22 * np.abs(y)
     return y, tol
 
 
