@@ -14,6 +14,7 @@ import torch
 from ._lib import lib
 
 __all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual", "fp8_quantize_dual_bias_grad",
+           "fp8_quantize_dual_bias_grad_noalloc", "NOALLOC_SCRATCH_BYTES",
            "fp8_quantize_dynamic", "DYNAMIC_WORKSPACE_BYTES", "fp8_amax_fold", "fp8_mm", "fp8_mm_ex", "FP8_E4M3", "FP8_E5M2", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
 
 E4M3, E5M2 = 0, 1
@@ -25,6 +26,7 @@ _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
 RING_SCRATCH_WORDS = 1024  # FP8MI_RING_SCRATCH_WORDS
 DYNAMIC_WORKSPACE_BYTES = 4096  # FP8MI_DYNAMIC_WORKSPACE_BYTES
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024  # FP8MI_NOALLOC_SCRATCH_BYTES
 LAYOUT_ROW, LAYOUT_T, LAYOUT_DUAL = 0, 1, 2
 
 
@@ -257,6 +259,33 @@ def fp8_quantize_dual_bias_grad(dy: torch.Tensor, fmt, out_row: torch.Tensor | N
                                              _ptr(out_t), ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out),
                                              _ptr(amax_out), _ptr(bias_grad_out), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(dy)))
+    return out_row, out_t, bias_grad_out
+
+
+def fp8_quantize_dual_bias_grad_noalloc(dy: torch.Tensor, fmt, out_row: torch.Tensor, out_t: torch.Tensor,
+                                        bias_grad_out: torch.Tensor, scale: torch.Tensor | None = None,
+                                        ring: torch.Tensor | None = None, scale_inv_out: torch.Tensor | None = None,
+                                        amax_out: torch.Tensor | None = None):
+    """fp8_quantize_dual_bias_grad with the library's own scratch instead of a
+    workspace: every output is the caller's (nothing is allocated here or in
+    the library).  Returns (codes, codes_t, bias_grad)."""
+    if dy.dim() != 2 or (dy.shape[1] > 1 and dy.stride(1) != 1):
+        raise ValueError("dy must be 2-D with unit column stride")
+    rows, cols = dy.shape
+    f = _fmt(fmt)
+    out_row, out_t = _as_codes(out_row, "out_row"), _as_codes(out_t, "out_t")
+    dt = _quant_checks(dy, "dy", out_row, out_t, scale, scale_inv_out, amax_out)
+    _vector(bias_grad_out, cols, "bias_grad_out")
+    if bias_grad_out.dtype != torch.bfloat16:
+        raise ValueError("bias_grad_out must be bfloat16")
+    ld_x = dy.stride(0) if rows > 1 else cols
+    ld_r = out_row.stride(0) if out_row.shape[0] > 1 else out_row.shape[1]
+    ld_t = out_t.stride(0) if out_t.shape[0] > 1 else out_t.shape[1]
+    rp, h = _ring_args(ring)
+    _on_device(dy, out_row, out_t, scale, ring, scale_inv_out, amax_out, bias_grad_out)
+    _check(lib().fp8_quantize_dual_bias_grad_noalloc(_ptr(dy), dt, rows, cols, ld_x, f, _ptr(out_row), ld_r,
+                                                     _ptr(out_t), ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out),
+                                                     _ptr(amax_out), _ptr(bias_grad_out), _stream(dy)))
     return out_row, out_t, bias_grad_out
 
 

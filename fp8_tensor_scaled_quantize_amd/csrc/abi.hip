@@ -110,10 +110,10 @@ static fp8mi_status check_outputs(int mode, int64_t rows, int64_t cols, const ui
   return FP8MI_OK;
 }
 
-static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
-                                    int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
-                                    const float* scale, uint32_t* ring, int32_t H, float* scale_inv_out,
-                                    float* amax_out, void* stream, double* bias_ws = nullptr) {
+static fp8mi_status check_quantize(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                                   int mode, const uint8_t* out_row, int64_t ld_row, const uint8_t* out_t,
+                                   int64_t ld_t, const float* scale, uint32_t* ring, int32_t H,
+                                   const float* scale_inv_out, const float* amax_out) {
   fp8mi_status s = check_input(x, dt, rows, cols, ld_x);
   if (s != FP8MI_OK) return s;
   if (!valid_fmt(fmt)) return fail(FP8MI_ERR_ENUM, "fmt %d is not FP8MI_E4M3/FP8MI_E5M2", fmt);
@@ -122,25 +122,71 @@ static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t
   s = check_outputs(mode, rows, cols, out_row, ld_row, out_t, ld_t, scale_inv_out, amax_out);
   if (s != FP8MI_OK) return s;
   if (reinterpret_cast<uintptr_t>(scale) & 3u) return fail(FP8MI_ERR_ARG, "fp32 scalars must be 4-byte aligned");
+  return FP8MI_OK;
+}
+
+static fp8mi_status quantize_common(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                                    int mode, uint8_t* out_row, int64_t ld_row, uint8_t* out_t, int64_t ld_t,
+                                    const float* scale, uint32_t* ring, int32_t H, float* scale_inv_out,
+                                    float* amax_out, void* stream, double* bias_ws = nullptr) {
+  fp8mi_status s = check_quantize(x, dt, rows, cols, ld_x, fmt, mode, out_row, ld_row, out_t, ld_t, scale, ring, H,
+                                  scale_inv_out, amax_out);
+  if (s != FP8MI_OK) return s;
   hipError_t e = launch_quantize(x, dt, rows, cols, ld_x, fmt, mode, out_row, ld_row, out_t, ld_t, scale, ring, H,
                                  scale_inv_out, amax_out, static_cast<hipStream_t>(stream), bias_ws);
   return from_hip(e, "quantize launch");
 }
 
-// Bias-gradient arguments shared by fp8_bias_grad and the fused dual quantize.
-static fp8mi_status check_bias_grad(int dt, int64_t rows, int64_t cols, const void* out, const void* workspace,
-                                    size_t workspace_bytes) {
+// Bias-gradient arguments shared by fp8_bias_grad and the fused dual
+// quantizes, apart from the workspace.
+static fp8mi_status check_bias_grad_args(int dt, int64_t rows, int64_t cols, const void* out) {
   if (dt == FP8MI_F32) return fail(FP8MI_ERR_UNSUPPORTED, "the bias gradient takes bf16 or fp16 gradients");
   if (cols > 0 && !out) return fail(FP8MI_ERR_NULL, "bias gradient output is NULL");
   if (reinterpret_cast<uintptr_t>(out) & 1u) return fail(FP8MI_ERR_ARG, "bias gradient output must be 2-byte aligned");
+  if ((cols + 511) / 512 > 0x7FFFFFFF || (rows + 127) / 128 > 65535)
+    return fail(FP8MI_ERR_UNSUPPORTED, "rows=%lld cols=%lld beyond the launch grid", (long long)rows,
+                (long long)cols);
+  return FP8MI_OK;
+}
+
+static fp8mi_status check_bias_grad(int dt, int64_t rows, int64_t cols, const void* out, const void* workspace,
+                                    size_t workspace_bytes) {
+  fp8mi_status s = check_bias_grad_args(dt, rows, cols, out);
+  if (s != FP8MI_OK) return s;
   const size_t need = (size_t)grad_bias_workspace_bytes(rows, cols);
   if (need > 0 && !workspace) return fail(FP8MI_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
   if (workspace_bytes < need)
     return fail(FP8MI_ERR_ARG, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 7u) return fail(FP8MI_ERR_ARG, "workspace must be 8-byte aligned");
-  if ((cols + 511) / 512 > 0x7FFFFFFF || (rows + 127) / 128 > 65535)
-    return fail(FP8MI_ERR_UNSUPPORTED, "rows=%lld cols=%lld beyond the launch grid", (long long)rows,
-                (long long)cols);
+  return FP8MI_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch of fp8_quantize_dual_bias_grad_noalloc: the per-tile
+// fp64 column sums that fp8_quantize_dual_bias_grad keeps in the caller's
+// workspace.  Every device the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) double scratch[FP8MI_NOALLOC_SCRATCH_BYTES / sizeof(double)];
+
+static fp8mi_status scratch_of_current_device(double** out) {
+  static std::mutex mu;
+  static std::vector<double*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(FP8MI_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    addr[dev] = static_cast<double*>(p);
+  }
+  *out = addr[dev];
   return FP8MI_OK;
 }
 
@@ -202,6 +248,37 @@ fp8mi_status fp8_quantize_dual_bias_grad(const void* x, int x_dtype, int64_t row
   if (s != FP8MI_OK || cols == 0) return s;
   return from_hip(launch_grad_bias_finalize(static_cast<const double*>(workspace), rows, cols,
                                             static_cast<uint16_t*>(bias_grad_out), static_cast<hipStream_t>(stream)),
+                  "bias grad finalize launch");
+}
+
+fp8mi_status fp8_quantize_dual_bias_grad_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                                 int64_t ld_x, int fmt, uint8_t* out_row, int64_t ld_row,
+                                                 uint8_t* out_t, int64_t ld_t, const float* scale, uint32_t* ring,
+                                                 int32_t hist_len, float* scale_inv_out, float* amax_out,
+                                                 void* bias_grad_out, void* stream) {
+  if (!valid_dtype(x_dtype)) return fail(FP8MI_ERR_ENUM, "x_dtype %d is not F32/F16/BF16", x_dtype);
+  fp8mi_status s = check_bias_grad_args(x_dtype, rows, cols, bias_grad_out);
+  if (s != FP8MI_OK) return s;
+  s = check_quantize(x, x_dtype, rows, cols, ld_x, fmt, 2, out_row, ld_row, out_t, ld_t, scale, ring, hist_len,
+                     scale_inv_out, amax_out);
+  if (s != FP8MI_OK) return s;
+  const size_t need = (size_t)grad_bias_workspace_bytes(rows, cols);
+  if (need > (size_t)FP8MI_NOALLOC_SCRATCH_BYTES)
+    return fail(FP8MI_ERR_UNSUPPORTED,
+                "rows=%lld cols=%lld need %zu bytes of bias-gradient scratch, above the library's %zu; "
+                "use fp8_quantize_dual_bias_grad with a caller workspace",
+                (long long)rows, (long long)cols, need, (size_t)FP8MI_NOALLOC_SCRATCH_BYTES);
+  double* ws = nullptr;
+  if (need > 0) {
+    s = scratch_of_current_device(&ws);
+    if (s != FP8MI_OK) return s;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  s = from_hip(launch_quantize(x, x_dtype, rows, cols, ld_x, fmt, 2, out_row, ld_row, out_t, ld_t, scale, ring,
+                               hist_len, scale_inv_out, amax_out, st, ws),
+               "quantize launch");
+  if (s != FP8MI_OK || cols == 0) return s;
+  return from_hip(launch_grad_bias_finalize(ws, rows, cols, static_cast<uint16_t*>(bias_grad_out), st),
                   "bias grad finalize launch");
 }
 

@@ -276,6 +276,29 @@ FP8MI_API fp8mi_status fp8_quantize_dual_bias_grad(const void* x, int x_dtype, i
                                                    void* stream);
 
 /*
+ * fp8_quantize_dual_bias_grad_noalloc -- fp8_quantize_dual_bias_grad for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving or training loops, harnesses that forbid allocation): the
+ * same arguments without the workspace, the same results bit for bit.  The
+ * per-tile column sums go to a scratch array the library owns, one per GPU,
+ * FP8MI_NOALLOC_SCRATCH_BYTES bytes, held from the first call on that GPU
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  A gradient whose sums need more than the
+ * array, fp8_bias_grad_workspace_bytes(rows, cols) >
+ * FP8MI_NOALLOC_SCRATCH_BYTES (8 MiB: ceil(rows / 128) * cols <= 1048576,
+ * e.g. 8192 x 6912 uses 3.5 MB), returns FP8MI_ERR_UNSUPPORTED before any
+ * launch.  Every call on one GPU shares its array, and nothing in it needs
+ * clearing (each call writes every sum it reads): calls that overlap on one
+ * GPU (different streams, or host threads without ordering) race.
+ */
+#define FP8MI_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+FP8MI_API fp8mi_status fp8_quantize_dual_bias_grad_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                                           int64_t ld_x, int fmt, uint8_t* out_row, int64_t ld_row,
+                                                           uint8_t* out_t, int64_t ld_t, const float* scale,
+                                                           uint32_t* ring, int32_t hist_len, float* scale_inv_out,
+                                                           float* amax_out, void* bias_grad_out, void* stream);
+
+/*
  * fp8_bias_grad -- bias gradient of an fp8 linear layer: out[j] = the sum of
  * dy[i, j] over all rows i (every leading dimension flattened into rows),
  * accumulated in fp64 in a fixed order and rounded once to bf16

@@ -247,6 +247,35 @@ def test_fused_dual_bias_grad_rejects(L):
     assert call(rows=-1) == SHAPE
 
 
+def test_noalloc_dual_bias_grad_rejects(L):
+    """The allocation-free fused call checks everything the workspace form
+    does, and rejects a gradient whose column sums exceed the library's
+    scratch (FP8MI_NOALLOC_SCRATCH_BYTES) -- all before any HIP call."""
+    f = L.fp8_quantize_dual_bias_grad_noalloc
+    ring, H = FAKE, 4
+
+    def call(x=FAKE, dt=2, rows=4, cols=4, ld=None, fmt=0, o_row=FAKE, o_t=FAKE, scale=None, ring=ring, h=H,
+             db=FAKE):
+        ld = cols if ld is None else ld
+        return f(x, dt, rows, cols, ld, fmt, o_row, cols, o_t, rows, scale, ring, h, None, None, db, None)
+
+    assert call(dt=0) == UNSUP          # fp32 gradient
+    assert call(dt=9) == ENUM
+    assert call(db=None) == NULL
+    assert call(db=FAKE + 1) == ARG
+    assert call(fmt=5) == ENUM
+    assert call(o_t=None) == NULL
+    assert call(rows=-1) == SHAPE
+    assert call(scale=FAKE) == ARG      # both scale and ring
+    cap = 8 * 1024 * 1024
+    header = open(os.path.join(ROOT, "include", "fp8mi.h")).read()
+    assert re.search(r"#define FP8MI_NOALLOC_SCRATCH_BYTES\s+\(8 \* 1024 \* 1024\)", header)
+    # ceil(rows / 128) * cols * 8 bytes: 2 tiles x 524288 columns fit exactly, one more column does not
+    assert L.fp8_bias_grad_workspace_bytes(256, 524288) == cap
+    assert call(rows=256, cols=524289) == UNSUP
+    assert b"scratch" in L.fp8mi_last_error()
+
+
 def test_ring_seed_rejects(L):
     f = L.fp8_ring_seed
     assert f(None, 4, FAKE, 0, None) == NULL
