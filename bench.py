@@ -48,14 +48,44 @@ def parse():
                     help="skip the other configs' shapes (profiling runs of the headline kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--launches", type=int, default=0,
+                    help="back-to-back launches per headline kernel (default max(10, steps))")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-kernel call counts, mean and median durations of a rocprofv3 "
+                         "kernel-trace CSV and exit (no GPU use)")
     return ap.parse_args()
 
 
+_POOL_X = None
+
+
+def _pool_init():
+    """Process-pool worker set-up: the same seeded bf16 tensor as the
+    single-core leg, generated in the worker (nothing large is pickled)."""
+    global _POOL_X
+    import synth
+    _POOL_X = synth.gaussian(QSHAPE, 1.0, "bf16", 90, 4)
+
+
+def _quantize_block(bounds):
+    """One process-pool task: the oracle's dual-layout quantize of a row block
+    (row and transposed codes); returns the block's raw amax, whose maximum
+    over the blocks the caller folds."""
+    import oracle as O
+    i0, i1 = bounds
+    return O.quantize(_POOL_X[i0:i1], "bf16", O.E4M3, scale=1.0)["amax"]
+
+
 def cpu_baseline(seconds_target=6.0):
-    """The CPU oracle on a bounded sample of the same workload: the GEMM on a
-    block of output rows of the 4096^3 problem (up to the whole problem), and
-    the dual-layout quantize of the 8192x1536 tensor, each repeated until
-    about seconds_target of CPU time so the rate is stable."""
+    """The CPU oracle on a bounded sample of the same workload, timed on this
+    host: the GEMM on a block of output rows of the 4096^3 problem (up to the
+    whole problem; float64 BLAS on its own threads), and the dual-layout
+    quantize of the 8192x1536 tensor, once on one core and once as a process
+    pool over row blocks on every core this process may use.  Each leg repeats
+    until about seconds_target of time so its rate is stable, and reports the
+    cores it used."""
+    import multiprocessing as mp
+
     import numpy as np
     import oracle as O
     import synth
@@ -87,19 +117,124 @@ def cpu_baseline(seconds_target=6.0):
         mm_s += time.perf_counter() - t0
         mm_runs += 1
     mm_tflops = 2.0 * rows * N * K * mm_runs / mm_s / 1e12
-    qrows = QSHAPE[0]
-    x = synth.gaussian((qrows, QSHAPE[1]), 1.0, "bf16", 90, 4)
+    qrows, qcols = QSHAPE
+    x = synth.gaussian((qrows, qcols), 1.0, "bf16", 90, 4)
+    qbytes = qrows * qcols * (2 + 2)
     q_runs, q_s = 0, 0.0
     while q_s < seconds_target:
         t2 = time.perf_counter()
         O.quantize(x, "bf16", O.E4M3, ring=O.Ring.new(HIST, 1.0))
         q_s += time.perf_counter() - t2
         q_runs += 1
-    q_gbs = qrows * QSHAPE[1] * (2 + 2) * q_runs / q_s / 1e9
+    # the same quantize over row blocks in a process pool: fresh interpreters
+    # (spawn), one per usable core up to 16 (the host share of one GPU)
+    pool_cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    step_rows = -(-qrows // pool_cores)
+    blocks = [(i, min(i + step_rows, qrows)) for i in range(0, qrows, step_rows)]
+    with mp.get_context("spawn").Pool(pool_cores, initializer=_pool_init) as pool:
+        pool.map(_quantize_block, blocks)  # workers started and warm
+        p_runs, p_s = 0, 0.0
+        while p_s < seconds_target:
+            t3 = time.perf_counter()
+            amaxes = pool.map(_quantize_block, blocks)
+            O.fold(O.Ring.new(HIST, 1.0), np.float32(max(amaxes)), O.E4M3)
+            p_s += time.perf_counter() - t3
+            p_runs += 1
     return {"value": round(mm_tflops, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"GEMM: {rows} output rows of {M}x{N}x{K} (float64 BLAS + bf16 rounding), {mm_runs} runs, "
-                      f"{mm_s:.1f} s; quantize dual: {qrows}x{QSHAPE[1]} bf16, {q_runs} runs, {q_s:.1f} s",
-            "quantize_GBps": round(q_gbs, 4), "host_cpus": len(os.sched_getaffinity(0))}
+            "sample": f"GEMM: {rows} output rows of {M}x{N}x{K} (float64 BLAS on {blas_threads} threads + bf16 "
+                      f"rounding), {mm_runs} runs, {mm_s:.1f} s; quantize dual {qrows}x{qcols} bf16: one core "
+                      f"{q_runs} runs {q_s:.1f} s, process pool of {pool_cores} over {len(blocks)} row blocks "
+                      f"{p_runs} runs {p_s:.1f} s",
+            "quantize": {"GBps_1core": round(qbytes * q_runs / q_s / 1e9, 4), "cores_1core": 1,
+                         "GBps_pool": round(qbytes * p_runs / p_s / 1e9, 4), "cores_pool": pool_cores,
+                         "unit": "GB/s", "algorithmic_bytes": qbytes},
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def trace_summary(path):
+    """Per (kernel, grid) call count, mean and median duration (us) from a
+    rocprofv3 --kernel-trace CSV: the profiler's own clock, one row per
+    launch.  Prints a table; kernels are named up to their template arguments."""
+    import csv
+    import re
+    import statistics
+    groups, lib_names = {}, set()
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "")
+            m = re.search(r"(\w+<[^()]*>|\w+)\(", name)
+            short = m.group(1) if m else name.split("(")[0]
+            short = re.sub(r"\(fp8mi::\w+\)", "", short).replace("fp8mi::", "")
+            grid = int(row.get("Grid_Size_X", row.get("Grid_Size", 0)) or 0) * \
+                int(row.get("Grid_Size_Y", 1) or 1) * int(row.get("Grid_Size_Z", 1) or 1)
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            groups.setdefault((short, grid), []).append(dur)
+            if "fp8mi::" in name:
+                lib_names.add(short)
+    print(f"{'kernel':48s} {'grid':>8s} {'calls':>5s} {'mean':>8s} {'median':>8s} {'min':>8s} {'max':>8s}")
+    # the library's kernels only (torch's input generation and copies are not part of the path)
+    ours = {k: v for k, v in groups.items() if k[0] in lib_names}
+    for (k, g), v in sorted(ours.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{k:48s} {g:8d} {len(v):5d} {statistics.fmean(v):8.2f} {statistics.median(v):8.2f} "
+              f"{min(v):8.2f} {max(v):8.2f}")
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi, in-process) in a background
+    thread while timed work runs: the MFMA peak assumes 2.4 GHz, and the
+    chip lowers its clock under sustained load."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+        self.samples, self.avg_samples, self.error, self.period = [], [], None, period_s
+        self._stop, self._ready = threading.Event(), threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            try:
+                h = amdsmi.amdsmi_get_processor_handles()[0]
+                self._ready.set()
+                while not self._stop.is_set():
+                    # the SMU's gpu-metrics table: one current graphics clock per XCD (MHz)
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+                    if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+                        clks = [m["current_gfxclk"]]
+                    if clks:
+                        self.samples.append(sum(clks) / len(clks))
+                    avg = m.get("average_gfxclk_frequency")
+                    if isinstance(avg, (int, float)) and avg > 0:
+                        self.avg_samples.append(float(avg))
+                    time.sleep(self.period)
+            finally:
+                amdsmi.amdsmi_shut_down()
+        except Exception as e:  # no SMI access on this host: report why
+            self.error = f"{type(e).__name__}: {e}"[:200]
+        finally:
+            self._ready.set()
+
+    def __enter__(self):
+        self._thread.start()
+        self._ready.wait(timeout=10)
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def summary(self):
+        import statistics
+        src = "amdsmi gpu metrics: current_gfxclks (mean over XCDs), average_gfxclk_frequency"
+        if not self.samples:
+            return {"source": src, "error": self.error or "no samples"}
+        out = {"source": src, "samples": len(self.samples), "median_MHz": statistics.median(self.samples),
+               "min_MHz": min(self.samples), "max_MHz": max(self.samples)}
+        if self.avg_samples:
+            out["average_gfxclk_median_MHz"] = statistics.median(self.avg_samples)
+        return out
 
 
 # host-only argument validation: no kernel code, so not part of the hash
@@ -293,6 +428,9 @@ def sweep(torch, fp8mi, synth, dev, prime):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -365,7 +503,7 @@ def main():
         return e0.elapsed_time(e1) / n  # ms per call
 
     total_ms = timed(lambda i: step(args.warmup + i), args.steps) * args.steps
-    nlaunch = max(10, args.steps)
+    nlaunch = args.launches if args.launches > 0 else max(10, args.steps)
     names = ["quantize_row", "quantize_transposed", "quantize_dual", "mm_fp8", "quantize_dynamic_row",
              "quantize_dynamic_dual", "mm_fp8_out_e4m3", "mm_fp8_kmajor"]
     C8_out = torch.empty((M, N), dtype=torch.uint8, device=dev)
@@ -395,7 +533,23 @@ def main():
         "mm_fp8_kmajor": lambda i: fp8mi.fp8_mm(A_km[i % nm].t(), B_km[i % nm].t(), fp8mi.E4M3, fp8mi.E4M3, sa, sb,
                                                 bias, out=C_out),
     }
-    us = [timed(launches[nme], nlaunch) * 1e3 for nme in names]
+    us = []
+    clock = None
+    for nme in names:
+        if nme == "mm_fp8":
+            # sample the graphics clock over a longer run of the headline GEMM
+            with ClockSampler() as cs:
+                timed(launches[nme], 5000)
+            clock = cs.summary()
+        us.append(timed(launches[nme], nlaunch) * 1e3)
+    # practical HBM ceiling: the streaming reference kernel moving the same
+    # bytes as the row / transposed quantize (read 2 B, write 1 B per element)
+    # and as the dual quantize (read 2 B, write 2 B), over the same inputs
+    ref_row = torch.empty(R * C, dtype=torch.uint8, device=dev)
+    ref_dual = torch.empty(R * C * 2, dtype=torch.uint8, device=dev)
+    ceil_us = {"row": timed(lambda i: fp8mi.stream_reference(xq[i % nq], ref_row), nlaunch) * 1e3,
+               "dual": timed(lambda i: fp8mi.stream_reference(xq[i % nq], ref_dual), nlaunch) * 1e3}
+    del ref_row, ref_dual
     qbytes = {"quantize_row": R * C * 3, "quantize_transposed": R * C * 3, "quantize_dual": R * C * 4,
               "quantize_dynamic_row": R * C * 3, "quantize_dynamic_dual": R * C * 4}
     flops = 2.0 * M * N * K
@@ -409,6 +563,12 @@ def main():
                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": qbytes[nme]}
         if "dynamic" in nme:
             quant[nme]["note"] = "us per call = amax pass + quantize pass (two launches); bytes = one read + codes"
+        else:
+            c_us = ceil_us["dual" if nme.endswith("dual") else "row"]
+            quant[nme]["frac_of_stream_reference"] = round(c_us / float(us[i]), 4)
+    ceiling = {k: {"us_per_launch": round(v, 3), "GBps": round(R * C * (4 if k == "dual" else 3) / (v * 1e-6) / 1e9, 1),
+                   "frac_hbm_peak": round(R * C * (4 if k == "dual" else 3) / (v * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+               for k, v in ceil_us.items()}
 
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -440,7 +600,10 @@ def main():
                      "algorithmic_flops": flops},
         "roofline_quantize": {"bound": "hbm", "achieved": quant["quantize_dual"]["GBps"], "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": quant["quantize_dual"]["frac_hbm_peak"], "traffic": None,
-                              "kernel": "quantize_dual"},
+                              "kernel": "quantize_dual",
+                              "stream_reference": dict(ceiling, note="fp8mi_stream_reference: the same bytes "
+                                                       "with the row quantize's access shape and no arithmetic")},
+        "gpu_clock_during_mm_fp8": clock,
         "quantize": quant,
         "mm_fp8_out_e4m3": {"us_per_launch": round(float(us[names.index("mm_fp8_out_e4m3")]), 3),
                             "TFLOPs": round(flops / (us[names.index("mm_fp8_out_e4m3")] * 1e-6) / 1e12, 1),

@@ -14,7 +14,7 @@ import torch
 from ._lib import lib
 
 __all__ = ["E4M3", "E5M2", "F32", "F16", "BF16", "Fp8Error", "fp8_quantize", "fp8_quantize_dual", "fp8_quantize_dual_bias_grad",
-           "fp8_quantize_dual_bias_grad_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "fp8_quantize_dual_bias_grad_noalloc", "NOALLOC_SCRATCH_BYTES", "stream_reference",
            "fp8_quantize_dynamic", "DYNAMIC_WORKSPACE_BYTES", "fp8_amax_fold", "fp8_mm", "fp8_mm_ex", "FP8_E4M3", "FP8_E5M2", "fp8_bias_grad", "fp8_bias_grad_workspace_bytes", "fp8_ring_seed", "new_ring", "ring_words", "version"]
 
 E4M3, E5M2 = 0, 1
@@ -23,7 +23,6 @@ FP8_E4M3, FP8_E5M2 = 3, 4  # fp8 storage types (fp8 bias / fp8 GEMM output of fp
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
-FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
 RING_SCRATCH_WORDS = 1024  # FP8MI_RING_SCRATCH_WORDS
 DYNAMIC_WORKSPACE_BYTES = 4096  # FP8MI_DYNAMIC_WORKSPACE_BYTES
 NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024  # FP8MI_NOALLOC_SCRATCH_BYTES
@@ -287,6 +286,19 @@ def fp8_quantize_dual_bias_grad_noalloc(dy: torch.Tensor, fmt, out_row: torch.Te
                                                      _ptr(out_t), ld_t, _ptr(scale), rp, h, _ptr(scale_inv_out),
                                                      _ptr(amax_out), _ptr(bias_grad_out), _stream(dy)))
     return out_row, out_t, bias_grad_out
+
+
+def stream_reference(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Measurement aid: fp8mi_stream_reference over two contiguous device
+    tensors (dst of src's byte size or its half) -- the HBM traffic of a
+    quantize moving the same bytes, with no arithmetic."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _on_device(src, dst)
+    _check(lib().fp8mi_stream_reference(src.data_ptr(), src.numel() * src.element_size(), dst.data_ptr(),
+                                        dst.numel() * dst.element_size(), _stream(src)))
+    return dst
 
 
 def fp8_quantize_dynamic(x: torch.Tensor, fmt, layout: int = LAYOUT_ROW, out_row: torch.Tensor | None = None,

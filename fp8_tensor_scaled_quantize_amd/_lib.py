@@ -26,6 +26,7 @@ SIGNATURES = {
     "fp8_bias_grad": (C.c_int, [_P, _I, _I64, _I64, _I64, _P, _P, C.c_size_t, _P]),
     "fp8_bias_grad_workspace_bytes": (C.c_size_t, [_I64, _I64]),
     "fp8_ring_seed": (C.c_int, [_P, _I32, _P, _I, _P]),
+    "fp8mi_stream_reference": (C.c_int, [_P, _I64, _P, _I64, _P]),
     "fp8mi_status_string": (C.c_char_p, [_I]),
     "fp8mi_last_error": (C.c_char_p, []),
     "fp8mi_version": (C.c_char_p, []),

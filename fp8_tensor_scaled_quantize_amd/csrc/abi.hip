@@ -420,6 +420,24 @@ fp8mi_status fp8_ring_seed(uint32_t* ring, int32_t hist_len, const float* amax, 
   return from_hip(launch_ring_seed(ring, hist_len, amax, fmt, static_cast<hipStream_t>(stream)), "seed launch");
 }
 
+fp8mi_status fp8mi_stream_reference(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
+                                    void* stream) {
+  if (src_bytes < 0 || src_bytes % 16) return fail(FP8MI_ERR_ARG, "src_bytes %lld is not a multiple of 16",
+                                                   (long long)src_bytes);
+  if (dst_bytes != src_bytes && 2 * dst_bytes != src_bytes)
+    return fail(FP8MI_ERR_ARG, "dst_bytes %lld must equal src_bytes %lld or its half", (long long)dst_bytes,
+                (long long)src_bytes);
+  if (src_bytes == 0) return FP8MI_OK;
+  if (!src || !dst) return fail(FP8MI_ERR_NULL, "src or dst is NULL");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u)
+    return fail(FP8MI_ERR_ARG, "src and dst must be 16-byte aligned");
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + (uintptr_t)dst_bytes && d0 < s0 + (uintptr_t)src_bytes)
+    return fail(FP8MI_ERR_ARG, "src and dst overlap");
+  return from_hip(launch_stream(src, src_bytes, dst, dst_bytes, static_cast<hipStream_t>(stream)),
+                  "stream reference launch");
+}
+
 const char* fp8mi_status_string(int s) {
   switch (s) {
     case FP8MI_OK: return "ok";

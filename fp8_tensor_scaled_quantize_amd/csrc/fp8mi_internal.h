@@ -83,5 +83,7 @@ hipError_t launch_grad_bias(const void* dy, int dt, int64_t rows, int64_t cols, 
 // Second half of the bias gradient: adds the per-chunk sums in chunk order, one bf16 rounding.
 hipError_t launch_grad_bias_finalize(const double* ws, int64_t rows, int64_t cols, uint16_t* out, hipStream_t st);
 hipError_t launch_ring_seed(uint32_t* ring, int H, const float* amax, int fmt, hipStream_t st);
+// Measurement aid (stream.hip): read src_bytes, write dst_bytes (= src_bytes or its half).
+hipError_t launch_stream(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes, hipStream_t st);
 
 }  // namespace fp8mi

@@ -336,6 +336,19 @@ FP8MI_API size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols);
  */
 FP8MI_API fp8mi_status fp8_ring_seed(uint32_t* ring, int32_t hist_len, const float* amax, int fmt, void* stream);
 
+/*
+ * fp8mi_stream_reference -- measurement aid, not part of the method: reads
+ * src_bytes of src and writes dst_bytes of dst with the row quantize's access
+ * shape and no arithmetic, so its time is the practical HBM ceiling for a
+ * quantize moving the same bytes (row / transposed: dst_bytes = src_bytes / 2
+ * for a 16-bit input; dual: dst_bytes = src_bytes).  dst receives bytes of src
+ * (the top byte of every 16-bit pair, or src itself).  src and dst: device,
+ * 16-byte aligned, not overlapping; src_bytes a multiple of 16; dst_bytes
+ * equal to src_bytes or to its half, else FP8MI_ERR_ARG.  One launch.
+ */
+FP8MI_API fp8mi_status fp8mi_stream_reference(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
+                                              void* stream);
+
 /* Static text of a status code. */
 FP8MI_API const char* fp8mi_status_string(int status);
 /* Thread-local detail of the last non-OK status returned on this thread. */

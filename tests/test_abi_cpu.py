@@ -32,7 +32,7 @@ def L():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"fp8_quantize", "fp8_quantize_dual", "fp8_amax_fold", "fp8_mm",
-                          "fp8mi_status_string", "fp8mi_last_error", "fp8mi_version"} | set(
+                          "fp8mi_status_string", "fp8mi_last_error", "fp8mi_version", "fp8mi_stream_reference"} | set(
         n for n in names if n.startswith("fp8_"))
 
 
@@ -274,6 +274,16 @@ def test_noalloc_dual_bias_grad_rejects(L):
     assert L.fp8_bias_grad_workspace_bytes(256, 524288) == cap
     assert call(rows=256, cols=524289) == UNSUP
     assert b"scratch" in L.fp8mi_last_error()
+
+
+def test_stream_reference_rejects(L):
+    f = L.fp8mi_stream_reference
+    assert f(FAKE, 40, FAKE * 4, 20, None) == ARG      # src bytes not a multiple of 16
+    assert f(FAKE, 48, FAKE * 4, 16, None) == ARG      # dst neither src's size nor its half
+    assert f(None, 48, FAKE * 4, 48, None) == NULL
+    assert f(FAKE + 8, 48, FAKE * 4, 48, None) == ARG  # misaligned
+    assert f(FAKE, 64, FAKE + 32, 64, None) == ARG     # overlapping
+    assert f(None, 0, None, 0, None) == OK             # nothing to move
 
 
 def test_ring_seed_rejects(L):
