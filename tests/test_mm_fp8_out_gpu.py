@@ -280,3 +280,26 @@ def test_nan_and_inf_outputs_quantize():
     assert (want[~nan] == 0x7E).any() and (want[~nan] == 0xFE).any()      # both saturations occur
     assert f32_bits(amax_t) == as_bits(ref["amax"]) and f32_bits(sinv_t) == as_bits(ref["scale_inv"])
     assert np.array_equal(ring_state_words(ring), ref["ring"].words())
+
+
+@pytest.mark.parametrize("K", [32, 512], ids=["precise", "plain"])
+def test_ring_fold_over_many_workgroups(K):
+    """A ring-mode FP8-out GEMM over 4200 workgroups (4200 batches of 64 x 64,
+    one tile each; 131 members per fold slot): codes, amax, scale_inv and
+    ring words bit-exact on exact small-integer data."""
+    batch, M, N = 4200, 64, 64
+    a = make_int_codes((batch, M, K), O.E4M3, 43, K, 0)
+    b = make_int_codes((batch, N, K), O.E4M3, 43, K, 1)
+    sa, sb = 0.5, 0.25
+    ring0 = O.Ring.new(4, 1.0)
+    ring0.hist[:] = [30.0, 0.0, 1.0, 0.0]
+    ring0.scale, ring0.idx = np.float32(O.FMT_MAX[O.E4M3] / 64.0), 3
+    ref = O.mm_quantized(a, O.E4M3, b, O.E4M3, O.E4M3, sa, sb, None, ring=ring0)
+    ring = ring_from_oracle(ring0)
+    sinv_t, amax_t = scalar(-1), scalar(-1)
+    out = fp8mi.fp8_mm_ex(to_dev_codes(a), to_dev_codes(b), 0, 0, scalar(sa), scalar(sb), out_fmt=0,
+                          out_ring=ring, out_scale_inv=sinv_t, out_amax=amax_t)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref["codes"])
+    assert f32_bits(amax_t) == as_bits(ref["amax"]) and f32_bits(sinv_t) == as_bits(ref["scale_inv"])
+    assert np.array_equal(ring_state_words(ring), ref["ring"].words())
