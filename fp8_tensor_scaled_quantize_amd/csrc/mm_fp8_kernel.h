@@ -248,8 +248,25 @@ __device__ __forceinline__ void tile_coords(int64_t wg64, int64_t tiles_m64, int
 
 // LAY: bit 0 -- A given K-major ([K, M], lda >= M), bit 1 -- B given K-major
 // ([K, N], ldb >= N); otherwise the operand is [rows, K] (NT).
-// PREC: the precise accumulation above (short K).
-template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS, int OUT, int LAY, bool PREC>
+// Wait until at most r steps of LPW loads each are outstanding (r in [0, MAXR]).
+template <int LPW, int MAXR> __device__ __forceinline__ void wait_steps(int r) {
+  if constexpr (MAXR > 0) {
+    if (r >= MAXR) {
+      wait_vmem_n<LPW * MAXR>();
+      return;
+    }
+    wait_steps<LPW, MAXR - 1>(r);
+  } else {
+    wait_vmem();
+  }
+}
+
+// PREC: the precise accumulation above (short K).  DEEP > 0: that many LDS
+// stages (DEEP - 1 steps of loads in flight) for the small tiles of
+// problems that leave CUs idle, where each workgroup's chain of load
+// latencies sets the time.
+template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS, int OUT, int LAY, bool PREC,
+          int DEEP = 0>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma(MmArgs p, int64_t tiles_m,
                                                                                  int64_t tiles_n, int group_m) {
   constexpr bool KMA = (LAY & 1) != 0, KMB = (LAY & 2) != 0;
@@ -266,7 +283,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
   // 64 x 128 tile (24 KiB per stage, two workgroups per CU) keeps three, so
   // two K steps of loads are in flight -- small and skinny problems, which
   // leave CUs idle and are bound by load latency, gain most from it
-  constexpr int STAGES = BM * BN <= 64 * 128 ? 3 : 2;
+  constexpr int STAGES = DEEP > 0 ? DEEP : (BM * BN <= 64 * 128 ? 3 : 2);
+  static_assert(DEEP == 0 || (DEEP >= 3 && BM * BN <= 64 * 128), "deep pipelines are for the small tiles");
   constexpr int LPW = LA + LB;  // load instructions per wave and K step
   constexpr int SMEM = STAGES * STAGE > BM * CROW * 2 ? STAGES * STAGE : BM * CROW * 2;
   __shared__ __align__(16) uint8_t smem[SMEM];
@@ -471,12 +489,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue_all(s, s * kBK);
-  if constexpr (STAGES == 3) {
-    if (nk > 1) wait_vmem_n<LPW>();
-    else wait_vmem();
-  } else {
-    wait_vmem();
-  }
+  // step 0 must have landed; steps 1 .. min(STAGES - 2, nk - 1) may stay in flight
+  wait_steps<LPW, STAGES - 2>(nk - 1 < STAGES - 2 ? nk - 1 : STAGES - 2);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const uint8_t* As = smem + (kt % STAGES) * STAGE;
@@ -494,12 +508,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 #pragma unroll
       for (int j = 0; j < TJ; ++j) acc[i][j] = mma<FA, FB, PREC>(bfr[j], af, acc[i][j]);
     }
-    // step kt + 1 must have landed; step kt + 2's loads may stay in flight
-    if constexpr (STAGES == 3) {
-      if (kt + 2 < nk) wait_vmem_n<LPW>();
-      else wait_vmem();
-    } else {
-      wait_vmem();
+    // step kt + 1 must have landed; the loads of steps kt + 2 .. (those
+    // issued) may stay in flight
+    {
+      const int r = nk - 2 - kt;
+      wait_steps<LPW, STAGES - 2>(r < 0 ? 0 : (r < STAGES - 2 ? r : STAGES - 2));
     }
     __syncthreads();
   }
@@ -652,26 +665,33 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
 // 128x128 is reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128
 // kernel remains for operands whose byte extent does not fit a 32-bit buffer
 // offset.
-template <int FA, int FB, int BM, int BN, int WM_, int WN_, int MINB, int OUT, int LAY = 0, bool PREC = false>
+template <int FA, int FB, int BM, int BN, int WM_, int WN_, int MINB, int OUT, int LAY = 0, bool PREC = false,
+          int DEEP = 0>
 static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
   const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
-  hipLaunchKernelGGL((mm_fp8_dma<FA, FB, BM, BN, WM_, WN_, MINB, OUT, LAY, PREC>), grid, dim3(64 * WM_ * WN_), 0, st,
-                     p, tiles_m, tiles_n, 4);
+  hipLaunchKernelGGL((mm_fp8_dma<FA, FB, BM, BN, WM_, WN_, MINB, OUT, LAY, PREC, DEEP>), grid, dim3(64 * WM_ * WN_),
+                     0, st, p, tiles_m, tiles_n, 4);
   return hipGetLastError();
 }
 
 static inline int pick_tile(const MmArgs& p, int ncu) {
-  static const int forced = env_int_in("FP8MI_MM_TILE", 0, 5, -1);
+  static const int forced = env_int_in("FP8MI_MM_TILE", 0, 6, -1);
   if (forced >= 0 && forced != 4) return forced;
   const int64_t tm = (p.M + 255) / 256;
   const int64_t t256 = tm * ((p.N + 255) / 256) * p.batch, t192 = tm * ((p.N + 191) / 192) * p.batch;
   if (10 * (t256 > t192 ? t256 : t192) < 6 * (int64_t)ncu) {
     // small problems: 64 x 128 tiles, or 64 x 64 when even those would not
     // give every CU one (skinny shapes; measured 3-10% faster there, slower
-    // once the 64 x 128 tiles fill the chip)
+    // once the 64 x 128 tiles fill the chip); with at most one 64 x 64 tile
+    // per CU and a long K, its deep-pipeline form (8 stages, one workgroup
+    // per CU: 64x8192x2048 8.13 -> 7.97 us, 128x4096x4096 12.5 -> 11.7 us; a
+    // 6-stage 64 x 128 form was slower on every sweep shape)
     const int64_t t128 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
-    return t128 <= (int64_t)ncu ? 5 : 2;
+    const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch;
+    const bool long_k = p.K >= 6 * kBK;
+    if (t128 <= (int64_t)ncu) return long_k && t64 <= (int64_t)ncu ? 6 : 5;
+    return 2;
   }
   // per-CU time of the big-tile family: rounds of workgroups x the time of
   // one round, a 256 x 192 round taking ~0.9 of a 256 x 256 one (measured
@@ -692,6 +712,7 @@ template <int FA, int FB, int OUT, int LAY = 0> static hipError_t launch_dma_fam
     case 3: return launch_dma<FA, FB, 256, 192, 2, 4, 1, OUT, LAY>(p, st);
     case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2, OUT, LAY>(p, st);
     case 5: return launch_dma<FA, FB, 64, 64, 1, 4, 2, OUT, LAY>(p, st);
+    case 6: return launch_dma<FA, FB, 64, 64, 1, 4, 1, OUT, LAY, false, 8>(p, st);
     default: return launch_dma<FA, FB, 64, 128, 1, 4, 2, OUT, LAY>(p, st);
   }
 }

@@ -1,8 +1,8 @@
 """The library's tuning overrides (FP8MI_MM_TILE, FP8MI_Q_BPC,
 FP8MI_AMAX_BPC) are read once per process: a child process with malformed or
-out-of-range values (which the library ignores) and one with a valid forced
-GEMM tile must produce, bit for bit, what this process produces with the
-defaults -- a persistent-grid dual quantize (bf16 8192x6912, E5M2, ring), a
+out-of-range values (which the library ignores) and ones with a valid forced
+GEMM tile (128 x 128, and the deep-pipeline 64 x 64) must
+produce, bit for bit, what this process produces with the defaults -- a persistent-grid dual quantize (bf16 8192x6912, E5M2, ring), a
 current-scaling quantize (bf16 8192x1536) and a 2048x1536x6912 GEMM with bias
 (the result does not depend on the tile shape: every output's K sum runs in
 the same MFMA order)."""
@@ -53,6 +53,8 @@ def test_invalid_overrides_are_ignored_and_a_forced_tile_changes_nothing(tmp_pat
     ref = run_child(tmp_path, "default", {})
     bad = run_child(tmp_path, "bad", {"FP8MI_MM_TILE": "abc", "FP8MI_Q_BPC": "0", "FP8MI_AMAX_BPC": "-3"})
     tile = run_child(tmp_path, "tile1", {"FP8MI_MM_TILE": "1", "FP8MI_Q_BPC": "2"})
-    for other, tag in ((bad, "invalid overrides"), (tile, "forced tile 1, 2 workgroups per CU")):
+    deep64 = run_child(tmp_path, "tile6", {"FP8MI_MM_TILE": "6"})
+    for other, tag in ((bad, "invalid overrides"), (tile, "forced tile 1, 2 workgroups per CU"),
+                       (deep64, "forced deep-pipeline 64x64")):
         for k in ref:
             assert torch.equal(other[k], ref[k]), (tag, k)
