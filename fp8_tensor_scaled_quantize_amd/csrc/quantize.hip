@@ -5,8 +5,9 @@
 // one tiled kernel serves the transposed layout ("layout 1") and the dual
 // layout ("layout 2"), handling odd widths and misaligned bases inside the
 // kernel; the elementwise (row) quantize is a separate streaming kernel.
-// log:tests/extension (the in-kernel ring fold commit): the last workgroup
-// folds amax into the history window and publishes the next scale.
+// log:tests/extension (the in-kernel ring fold commit): the history update
+// and the next scale are computed inside the quantize launch, by whichever
+// workgroup completes last, instead of by separate kernels.
 // log:csrc/kernels/fp8_mm.cu, commit 69f35c46e0: amax is taken from the raw
 // input, never from the scaled or encoded values.
 //

@@ -47,8 +47,9 @@ def check(ref, o, ot, a, si, tag, pad=False):
 @pytest.mark.parametrize("dtype", O.DTYPES)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
 def test_dynamic_matrix(shape, dtype):
-    """13 shapes x 3 dtypes x 2 formats x 3 layouts x (aligned, misaligned
-    base, padded rows), byte-exact."""
+    """Current scaling over the same shape list, every input dtype, both
+    formats and the three layouts, each from an aligned base, a base one
+    element off and padded rows: codes, amax and 1/s equal the oracle's."""
     rows, cols = shape
     sid = SHAPES.index(shape)
     sigma = (1.0, 3e-3, 250.0)[sid % 3]

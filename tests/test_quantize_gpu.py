@@ -38,8 +38,10 @@ def run_layout(layout, xd, fmt_id, scale_t, misalign, rows, cols):
 @pytest.mark.parametrize("dtype", O.DTYPES)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
 def test_quantize_matrix(shape, dtype):
-    """13 shapes x 3 dtypes x 3 scales x 2 formats x 3 layouts x aligned /
-    misaligned, byte-exact (the analogue of the pages' golden-record matrix)."""
+    """Every combination of the shape list, input dtype, three scales, both
+    formats, the three layouts and an aligned or off-by-one-element base must
+    give the oracle's bytes exactly (the pages' quantize commits check their
+    kernels against stored records over a similar grid of cases)."""
     rows, cols = shape
     sid = SHAPES.index(shape)
     x = synth.gaussian(shape, 1.0, dtype, 2, synth.T_QUANT, sid, O.DTYPES.index(dtype))
