@@ -835,6 +835,12 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // persistent count for tuning.
 constexpr int kOneShotBlocksPerCU = 8;
 constexpr int kPersistBlocksPerCU = 3;
+// An explicit scale with amax_out: every workgroup's atomic max lands on the
+// caller's one word and these serialise (~12 ns each), so the row kernel
+// then runs persistent with one workgroup per CU (bf16 8192 x 1536: 27 ->
+// 12.3 us).  The tiled kernels keep their grids: persistent at one per CU
+// they were as slow (transposed 19.4 us) or slower (dual 23.2 against 21.8).
+constexpr int kAmaxOutBlocksPerCU = 1;
 
 template <int DT, int FMT, int M, bool BG, bool DYN>
 static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantArgs& p, int64_t tiles_c,
@@ -850,14 +856,16 @@ static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantAr
 template <int DT, int FMT, bool DYN>
 static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int ncu = device_cu_count();
-  static const int persist_bpc = env_int_in("FP8MI_Q_BPC", 1, 16, kPersistBlocksPerCU);
+  static const int persist_env = env_int_in("FP8MI_Q_BPC", 1, 16, kPersistBlocksPerCU);
+  const bool word_amax = !DYN && !p.ring && p.amax_out;  // one caller word takes every block's maximum
   const int64_t n = p.rows * p.cols;
   const bool contiguous_row = mode == kRow && p.ld_x == p.cols && p.ld_row == p.cols &&
                               (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 &&
                               (reinterpret_cast<uintptr_t>(p.out_row) & 15u) == 0;
   if (contiguous_row || n == 0) {
     const int64_t steps = cdiv(n, kFlatBlockStep);
-    if (steps <= (int64_t)ncu * kOneShotBlocksPerCU * kFlatUnroll) {
+    const int persist_bpc = word_amax ? kAmaxOutBlocksPerCU : persist_env;
+    if (!word_amax && steps <= (int64_t)ncu * kOneShotBlocksPerCU * kFlatUnroll) {
       const int64_t spb = kFlatUnroll, blocks = steps == 0 ? 1 : cdiv(steps, spb);
       hipLaunchKernelGGL((quantize_flat<DT, FMT, false, DYN>), dim3((unsigned)blocks), dim3(kFlatThreads), 0, st, p, n,
                          spb);
@@ -871,7 +879,7 @@ static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int64_t tiles_c = cdiv(p.cols, kTileC);
   const int64_t ntiles = cdiv(p.rows, kTileR) * tiles_c;
   const bool one_shot = ntiles <= (int64_t)ncu * kOneShotBlocksPerCU;
-  const int64_t tpb = one_shot ? 1 : cdiv(ntiles, (int64_t)ncu * persist_bpc);
+  const int64_t tpb = one_shot ? 1 : cdiv(ntiles, (int64_t)ncu * persist_env);
   const dim3 grid((unsigned)cdiv(ntiles, tpb));
   switch (mode) {
     case kRow: launch_tiled<DT, FMT, kRow, false, DYN>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
