@@ -3,9 +3,9 @@ FP8MI_AMAX_BPC) are read once per process: a child process with malformed or
 out-of-range values (which the library ignores) and ones with a valid forced
 GEMM tile (128 x 128, and the deep-pipeline 64 x 64) must
 produce, bit for bit, what this process produces with the defaults -- a persistent-grid dual quantize (bf16 8192x6912, E5M2, ring), a
-current-scaling quantize (bf16 8192x1536) and a 2048x1536x6912 GEMM with bias
-(the result does not depend on the tile shape: every output's K sum runs in
-the same MFMA order)."""
+current-scaling quantize (bf16 8192x1536), a 2048x1536x6912 GEMM with bias
+and an 8192x6912x1536 GEMM with bias (the result does not depend on the tile
+shape: every output's K sum runs in the same MFMA order)."""
 import os
 import subprocess
 import sys
@@ -34,8 +34,14 @@ a = fp8mi.fp8_quantize(dy[:2048].contiguous(), fp8mi.E4M3, scale=s)          # [
 b = fp8mi.fp8_quantize(dy[4096:5632].contiguous(), fp8mi.E4M3, scale=s)      # [1536, 6912]
 bias = synth.device_gaussian((1536,), 0.1, torch.bfloat16, 9802)
 y = fp8mi.fp8_mm(a, b, fp8mi.E4M3, fp8mi.E4M3, None, None, bias)
+# 8192 x 6912 x 1536: four rounds of 256 x 256 tiles by default
+a2 = fp8mi.fp8_quantize(x, fp8mi.E4M3, scale=s)                          # [8192, 1536]
+b2 = fp8mi.fp8_quantize(dy.t().contiguous()[:, :1536].contiguous(), fp8mi.E4M3, scale=s)  # [6912, 1536]
+bias2 = synth.device_gaussian((6912,), 0.1, torch.bfloat16, 9803)
+y2 = fp8mi.fp8_mm(a2, b2, fp8mi.E4M3, fp8mi.E4M3, None, None, bias2)
 torch.cuda.synchronize()
-torch.save({"q": q.cpu(), "qt": qt.cpu(), "ring": ring.cpu(), "d": d.cpu(), "y": y.cpu().view(torch.int16)}, sys.argv[2])
+torch.save({"q": q.cpu(), "qt": qt.cpu(), "ring": ring.cpu(), "d": d.cpu(), "y": y.cpu().view(torch.int16),
+            "y2": y2.cpu().view(torch.int16)}, sys.argv[2])
 '''
 
 

@@ -357,3 +357,29 @@ def test_short_k_gaussian_within_bound(K):
     every output within the stated bound, with a bias the size of the output."""
     run_case(512, 768, K, bias_kind="f32", key=90 + K, sample=512)
     run_case(512, 768, K, fa=O.E5M2, fb=O.E4M3, bias_kind="bf16", key=91 + K, sample=512)
+
+
+@pytest.mark.parametrize("layout,bias_dtype", [(0, "bf16"), (0, "f32"), (1, "f16")],
+                         ids=["nt-bf16", "nt-f32", "akm-f16"])
+def test_training_forward_shape_exact(layout, bias_dtype):
+    """8192 x 6912 x 1536 (the training forward): 864 tiles of 256 x 256, i.e.
+    three full rounds of workgroups and a fourth 37% full.  Exact
+    small-integer data: sampled rows bit-exact against the oracle with each
+    bias storage type and with A given K-major, plus every column around the
+    boundary between the 24th and 25th column tiles for the first 512 rows."""
+    M, N, K = 8192, 6912, 1536
+    a = make_int_codes((M, K), O.E4M3, 82, layout, 0)
+    b = make_int_codes((N, K), O.E4M3, 82, layout, 1)
+    bias_v = synth.rng(82, layout, 2).integers(-256, 257, size=N).astype(np.float32)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[bias_dtype]
+    bias_t = torch.from_numpy(bias_v).to(DEV).to(tdt)          # small integers: exact in every type
+    ad = to_dev_codes(a) if layout == 0 else to_dev_codes(np.ascontiguousarray(a.T)).t()
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    y = fp8mi.fp8_mm(ad, to_dev_codes(b), 0, 0, scalar(sa), scalar(sb), bias_t)
+    rows = sample_rows(M, 64, 82, layout, 3)
+    check(np_bf16_bits(y), a, O.E4M3, b, O.E4M3, sa, sb, bias_v.astype(np.float64), rows,
+          tag=f"forward {layout} {bias_dtype}", exact=True)
+    # and the columns around the 24th / 25th column-tile boundary, for every row of a few row tiles
+    got = np_bf16_bits(y)[:512, 6100:6200]
+    ref, _ = O.mm(a[:512], O.E4M3, b[6100:6200], O.E4M3, sa, sb, bias_v[6100:6200].astype(np.float64))
+    assert np.array_equal(got, ref[0])
