@@ -344,6 +344,21 @@ enum Mode : int { kRow = 0, kTrans = 1, kDual = 2 };
 
 __device__ __forceinline__ int lds_t_index(int c, int w) { return c * 32 + (w ^ (8 * ((c >> 3) & 3))); }
 
+// 4 x 4 byte transpose: words a, b, c, d hold 4 consecutive codes of rows 0..3;
+// col[k] receives byte k of each, row 0 in its low byte.  Two stages of
+// v_perm_b32 (byte k of the result picks byte sel_k of {hi, lo}, 0-3 from lo,
+// 4-7 from hi): interleave row pairs, then take the matching halves.
+__device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t (&col)[4]) {
+  const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
+  col[0] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);         // a0 b0 c0 d0
+  col[1] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);         // a1 b1 c1 d1
+  col[2] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);         // a2 b2 c2 d2
+  col[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);         // a3 b3 c3 d3
+}
+
 // One-shot form: each workgroup loads, encodes and stores its tiles in turn
 // (launched with one tile per workgroup; low registers, high occupancy).
 template <int DT, int FMT, int MODE, bool BG, bool DYN>
@@ -446,11 +461,11 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
     if constexpr (MODE == kTrans || MODE == kDual) {
       // 4x8 bytes -> 8 column words (rows 4rg..4rg+3 of column 8cg+e)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int h = e >> 2, sh = 8 * (e & 3);
-        const uint32_t col = ((rw[0][h] >> sh) & 0xFFu) | (((rw[1][h] >> sh) & 0xFFu) << 8) |
-                             (((rw[2][h] >> sh) & 0xFFu) << 16) | (((rw[3][h] >> sh) & 0xFFu) << 24);
-        lds_t[lds_t_index(8 * cg + e, rg)] = col;
+      for (int h = 0; h < 2; ++h) {
+        uint32_t col[4];
+        transpose4x4_bytes(rw[0][h], rw[1][h], rw[2][h], rw[3][h], col);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lds_t[lds_t_index(8 * cg + 4 * h + k, rg)] = col[k];
       }
       if constexpr (BG) {
         // bias gradient: fp64 column sums of the raw values -- this thread's 4
@@ -623,11 +638,11 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
     if constexpr (MODE == kTrans || MODE == kDual) {
       // 4x8 bytes -> 8 column words (rows 4rg..4rg+3 of column 8cg+e)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int h = e >> 2, sh = 8 * (e & 3);
-        const uint32_t col = ((rw[0][h] >> sh) & 0xFFu) | (((rw[1][h] >> sh) & 0xFFu) << 8) |
-                             (((rw[2][h] >> sh) & 0xFFu) << 16) | (((rw[3][h] >> sh) & 0xFFu) << 24);
-        lds_t[lds_t_index(8 * cg + e, rg)] = col;
+      for (int h = 0; h < 2; ++h) {
+        uint32_t col[4];
+        transpose4x4_bytes(rw[0][h], rw[1][h], rw[2][h], rw[3][h], col);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lds_t[lds_t_index(8 * cg + 4 * h + k, rg)] = col[k];
       }
       if constexpr (BG) {
         // bias gradient: fp64 column sums of the raw values -- this thread's 4
