@@ -344,6 +344,22 @@ enum Mode : int { kRow = 0, kTrans = 1, kDual = 2 };
 
 __device__ __forceinline__ int lds_t_index(int c, int w) { return c * 32 + (w ^ (8 * ((c >> 3) & 3))); }
 
+// Tile origin (row, column) of a tile index: 32-bit division whenever the
+// tile count fits (every tensor a GPU can hold), 64-bit otherwise; the
+// branch is uniform across the workgroup.
+__device__ __forceinline__ void tile_origin(int64_t tile, int64_t tiles_c, int64_t ntiles, int64_t& r0,
+                                            int64_t& c0) {
+  if (ntiles <= 0xFFFFFFFFll) {
+    const uint32_t t = (uint32_t)tile, tc = (uint32_t)tiles_c;
+    const uint32_t q = t / tc;
+    r0 = (int64_t)q * kTileR;
+    c0 = (int64_t)(t - q * tc) * kTileC;
+  } else {
+    r0 = (tile / tiles_c) * kTileR;
+    c0 = (tile % tiles_c) * kTileC;
+  }
+}
+
 // 4 x 4 byte transpose: words a, b, c, d hold 4 consecutive codes of rows 0..3;
 // col[k] receives byte k of each, row 0 in its low byte.  Two stages of
 // v_perm_b32 (byte k of the result picks byte sel_k of {hi, lo}, 0-3 from lo,
@@ -376,7 +392,8 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
   const int64_t t_first = (int64_t)blockIdx.x * tiles_per_block;
   const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
   for (int64_t tile = t_first; tile < t_last; ++tile) {
-    const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
+    int64_t r0, c0;
+    tile_origin(tile, tiles_c, ntiles, r0, c0);
     const int64_t cc = c0 + 8 * cg;  // this thread's first column
     float f[4][8];
     AbsMax<DT> am;
@@ -546,7 +563,8 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
   const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
 
   auto load_tile = [&](int64_t tile, TileRaw<DT>& L) {
-    const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
+    int64_t r0, c0;
+    tile_origin(tile, tiles_c, ntiles, r0, c0);
     const int64_t cc = c0 + 8 * cg;
     L.full = 0;
 #pragma unroll
@@ -560,7 +578,8 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
   };
 
   auto process_tile = [&](int64_t tile, const TileRaw<DT>& L, float s, bool sreg) {
-    const int64_t r0 = (tile / tiles_c) * kTileR, c0 = (tile % tiles_c) * kTileC;
+    int64_t r0, c0;
+    tile_origin(tile, tiles_c, ntiles, r0, c0);
     const int64_t cc = c0 + 8 * cg;  // this thread's first column
     float f[4][8];
     AbsMax<DT> am;
