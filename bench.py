@@ -48,11 +48,19 @@ def parse():
                     help="skip the other configs' shapes (profiling runs of the headline kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock-sampled run of the headline GEMM (counter-collection runs)")
     ap.add_argument("--launches", type=int, default=0,
                     help="back-to-back launches per headline kernel (default max(10, steps))")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-kernel call counts, mean and median durations of a rocprofv3 "
                          "kernel-trace CSV and exit (no GPU use)")
+    ap.add_argument("--mfma-summary", metavar="CSV",
+                    help="print the GEMM launches' MFMA utilisation from a rocprofv3 --pmc CSV of the MFMA / LDS "
+                         "counters and exit (no GPU use)")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a --calibrate-copy "
+                         "run into per-launch HBM bytes (OUT_JSON) and exit (no GPU use)")
     return ap.parse_args()
 
 
@@ -162,9 +170,7 @@ def trace_summary(path):
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
             name = row.get("Kernel_Name", "")
-            m = re.search(r"(\w+<[^()]*>|\w+)\(", name)
-            short = m.group(1) if m else name.split("(")[0]
-            short = re.sub(r"\(fp8mi::\w+\)", "", short).replace("fp8mi::", "")
+            short = _short_kernel(name)
             grid = int(row.get("Grid_Size_X", row.get("Grid_Size", 0)) or 0) * \
                 int(row.get("Grid_Size_Y", 1) or 1) * int(row.get("Grid_Size_Z", 1) or 1)
             dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
@@ -177,6 +183,91 @@ def trace_summary(path):
     for (k, g), v in sorted(ours.items(), key=lambda kv: -sum(kv[1])):
         print(f"{k:48s} {g:8d} {len(v):5d} {statistics.fmean(v):8.2f} {statistics.median(v):8.2f} "
               f"{min(v):8.2f} {max(v):8.2f}")
+
+
+# (kernel, grid threads) of the counted launches -> name in the bench line
+TRAFFIC_KERNELS = {
+    ("mm_fp8_dma<0, 0, 256, 256, 2, 4, 1, -1, 0, false, 0>", 131072): "mm_fp8",
+    ("mm_fp8_dma<0, 0, 256, 256, 2, 4, 1, 0, 0, false, 0>", 131072): "mm_fp8_out_e4m3",
+    ("mm_fp8_dma<0, 0, 256, 256, 2, 4, 1, -1, 3, false, 0>", 131072): "mm_fp8_kmajor",
+    ("quantize_flat<2, 0, false, false>", 393216): "quantize_row",
+    ("quantize_tiled<2, 0, 1, false, false>", 393216): "quantize_transposed",
+    ("quantize_tiled<2, 0, 2, false, false>", 393216): "quantize_dual",
+    ("quantize_flat<2, 0, false, true>", 393216): "quantize_dynamic_row_pass",
+    ("quantize_tiled<2, 0, 2, false, true>", 393216): "quantize_dynamic_dual_pass",
+    ("amax_partials<2>", 196864): "amax_pass_8192x1536",
+    ("stream_kernel<true>", 393216): "stream_reference_row_bytes",
+    ("stream_kernel<false>", 393216): "stream_reference_dual_bytes",
+    ("mm_fp8_dma<0, 0, 256, 256, 2, 4, 1, -1, 0, false, 0>", 442368): "training_forward_8192x6912x1536",
+    ("mm_fp8_dma<1, 0, 256, 192, 2, 4, 1, -1, 0, false, 0>", 131072): "training_dx_8192x1536x6912",
+    ("mm_fp8_dma<1, 0, 256, 192, 2, 4, 1, -1, 0, false, 0>", 110592): "training_dw_6912x1536x8192",
+    ("quantize_tiled_pf<2, 1, 2, true, false>", 196608): "training_dy_dual_bias_grad_8192x6912",
+}
+CALIBRATION_KERNEL = ("stream_kernel<false>", 8388608)   # 512 MiB copy: 2^29 bytes read and written
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"(\w+<[^()]*>|\w+)\(", name)
+    short = m.group(1) if m else name.split("(")[0]
+    return re.sub(r"\(fp8mi::\w+\)", "", short).replace("fp8mi::", "")
+
+
+def _counter_means(path, counter, lib_only=True):
+    """Mean value per dispatch of one counter, per (kernel, grid threads);
+    the library's kernels only unless lib_only is False."""
+    import csv
+    per_dispatch = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter or (lib_only and "fp8mi::" not in row["Kernel_Name"]):
+                continue
+            key = (_short_kernel(row["Kernel_Name"]), int(row.get("Grid_Size", 0) or 0))
+            d = per_dispatch.setdefault(key, {})
+            did = row.get("Dispatch_Id", row.get("Correlation_Id"))
+            d[did] = d.get(did, 0.0) + float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per_dispatch.items()}
+
+
+def traffic_summary(fetch_csv, write_csv, out_json):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> bytes per launch, scaled
+    by what the same counters read for the 512 MiB calibration copy."""
+    fetch, write = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    nbytes = float(1 << 29)
+    cal = {"fetch": fetch[CALIBRATION_KERNEL] * 1024 / nbytes, "write": write[CALIBRATION_KERNEL] * 1024 / nbytes}
+    kernels = {}
+    print(f"calibration (512 MiB copy): FETCH_SIZE reads {cal['fetch']:.4f} x, WRITE_SIZE {cal['write']:.4f} x its bytes")
+    print(f"{'kernel':52s} {'grid':>8s} {'fetch MB':>9s} {'write MB':>9s}  name")
+    for key in sorted(set(fetch) | set(write)):
+        fb = fetch.get(key, 0.0) * 1024 / cal["fetch"]
+        wb = write.get(key, 0.0) * 1024 / cal["write"]
+        name = TRAFFIC_KERNELS.get(key, "")
+        print(f"{key[0]:52s} {key[1]:8d} {fb / 1e6:9.2f} {wb / 1e6:9.2f}  {name}")
+        if name:
+            kernels[name] = {"fetch": fb, "write": wb, "grid": key[1]}
+    rec = {"source_sha256": kernel_source_hash(), "calibration": cal, "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                 "SQ_INSTS_LDS", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE")
+
+
+def mfma_summary(path, simds=1024, xcds=8):
+    """MFMA utilisation of the GEMM launches from a rocprofv3 --pmc CSV of
+    MFMA_COUNTERS: busy MFMA cycles per SIMD over the GPU-active cycles of one
+    XCD (GRBM_GUI_ACTIVE sums the XCDs)."""
+    vals = {c: _counter_means(path, c) for c in MFMA_COUNTERS}
+    for key in sorted(vals["SQ_VALU_MFMA_BUSY_CYCLES"]):
+        if not key[0].startswith("mm_fp8"):
+            continue
+        v = {c: vals[c].get(key, float("nan")) for c in MFMA_COUNTERS}
+        util = v["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / (v["GRBM_GUI_ACTIVE"] / xcds)
+        print(f"{key[0]} grid {key[1]:8d}: mfma_util {util:.3f}  "
+              f"lds_bank_conflict/lds_active {v['SQ_LDS_BANK_CONFLICT'] / v['SQ_LDS_IDX_ACTIVE']:.3f}  "
+              f"wait_inst_any/wave_cycles {v['SQ_WAIT_INST_ANY'] / v['SQ_WAVE_CYCLES']:.3f}")
+        print("    " + "  ".join(f"{c}={v[c]:.4g}" for c in sorted(MFMA_COUNTERS)))
 
 
 class ClockSampler:
@@ -431,6 +522,12 @@ def main():
     if args.trace_summary:
         trace_summary(args.trace_summary)
         return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -536,7 +633,7 @@ def main():
     us = []
     clock = None
     for nme in names:
-        if nme == "mm_fp8":
+        if nme == "mm_fp8" and not args.no_clock:
             # sample the graphics clock over a longer run of the headline GEMM
             with ClockSampler() as cs:
                 timed(launches[nme], 5000)
@@ -571,11 +668,13 @@ def main():
                for k, v in ceil_us.items()}
 
     if args.calibrate_copy:
+        # counter calibration: the streaming reference copying 512 MiB (reads and writes 2^29 bytes)
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            fp8mi.stream_reference(src, dst)
         torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": METRIC,
