@@ -559,8 +559,14 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
   const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
   float amax = 0.0f;
   const char* xb = static_cast<const char*>(p.x);
-  const int64_t t_first = (int64_t)blockIdx.x * tiles_per_block;
-  const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
+  // Tiles are dealt round-robin (tile b, b + grid, b + 2 grid, ...): at any
+  // time the workgroups work on one contiguous band of tiles, so the two
+  // 64-column halves of a row's 128-byte code lines are written at about the
+  // same time by neighbouring workgroups and leave the L2 as whole lines.
+  // (Contiguous runs of tiles per workgroup wrote 15% more bytes for the dual
+  // layout: the halves of a line split between runs were written far apart.)
+  (void)tiles_per_block;
+  const int64_t t_first = blockIdx.x, t_step = gridDim.x;
 
   auto load_tile = [&](int64_t tile, TileRaw<DT>& L) {
     int64_t r0, c0;
@@ -719,11 +725,11 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
   // while tile k is encoded and stored (the copy at the end of an iteration
   // waits only for that prefetch).
   TileRaw<DT> cur, nxt;
-  if (t_first < t_last) load_tile(t_first, cur);
+  if (t_first < ntiles) load_tile(t_first, cur);
   const float s = read_scale<FMT, DYN>(p);  // after the first loads are out
   const bool sreg = scale_regular(s);
-  for (int64_t tile = t_first; tile < t_last; ++tile) {
-    if (tile + 1 < t_last) load_tile(tile + 1, nxt);
+  for (int64_t tile = t_first; tile < ntiles; tile += t_step) {
+    if (tile + t_step < ntiles) load_tile(tile + t_step, nxt);
     process_tile(tile, cur, s, sreg);
     cur = nxt;
   }
@@ -914,6 +920,7 @@ static hipError_t launch_dt_fmt(const QuantArgs& p, int mode, hipStream_t st) {
   const int64_t ntiles = cdiv(p.rows, kTileR) * tiles_c;
   const bool one_shot = ntiles <= (int64_t)ncu * kOneShotBlocksPerCU;
   const int64_t tpb = one_shot ? 1 : cdiv(ntiles, (int64_t)ncu * persist_env);
+  // persistent: as many workgroups as before (ceil(ntiles / tpb)), tiles dealt round-robin
   const dim3 grid((unsigned)cdiv(ntiles, tpb));
   switch (mode) {
     case kRow: launch_tiled<DT, FMT, kRow, false, DYN>(one_shot, grid, st, p, tiles_c, ntiles, tpb); break;
