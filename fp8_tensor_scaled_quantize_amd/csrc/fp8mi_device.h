@@ -70,6 +70,20 @@ template <int FMT> __device__ __forceinline__ uint32_t cvt4(float a, float b, fl
   return (uint32_t)w;
 }
 
+// The same conversion without the clamp, for values already within
+// +-fmt_max (the conversion rounds those exactly).
+template <int FMT> __device__ __forceinline__ uint32_t cvt4_inrange(float a, float b, float c, float d) {
+  int w;
+  if constexpr (FMT == kE4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
+}
+
 // Integer saturating round-to-nearest-even encoder, used for words that hold
 // a NaN.  Normal range: drop the low fp32 mantissa bits with RNE (a carry
 // moves into the exponent field exactly as the format's code order does);

@@ -113,27 +113,6 @@ __device__ __forceinline__ float load_bias(const MmArgs& p, int64_t j, float bsc
   return decode_bias(p, load_bias_bits(p, j), bscale);
 }
 
-// Quantizing epilogue for 4 consecutive outputs of one row: y = acc * sab +
-// bias in fp32, codes enc(fl32(y * s)); `valid` masks which of the 4 count
-// toward the amax (NaN never does).  A NaN output takes the integer encoder
-// (the hardware conversion's NaN code differs), and so does every output
-// when the scale is not regular (scale_regular: y * s may be NaN for a
-// non-NaN y).
-template <int FMT>
-__device__ __forceinline__ uint32_t quant4(const v4f& acc, float sab, const float (&bv)[4], float s, bool sreg,
-                                           uint32_t valid, float& amax) {
-  float y[4];
-  bool nan = false;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    y[r] = fmaf(acc[r], sab, bv[r]);
-    nan |= y[r] != y[r];
-    if (((valid >> r) & 1u) && y[r] == y[r]) amax = fmaxf(amax, fabsf(y[r]));
-  }
-  if (nan || !sreg) return enc4_exact<FMT>(y[0] * s, y[1] * s, y[2] * s, y[3] * s);
-  return cvt4<FMT>(y[0] * s, y[1] * s, y[2] * s, y[3] * s);
-}
-
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma_nt(const v8i& bfrag, const v8i& afrag, const v4f& c) {
   // first operand: B rows (format FB -> cbsz), second: A rows (format FA -> blgp).
@@ -540,48 +519,100 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
     uint8_t* C = static_cast<uint8_t*>(p.c) + bz * p.stride_c;
     const float s_c = p.c_ring ? __uint_as_float(p.c_ring[p.c_H]) : *p.c_scale;
     const bool sreg = scale_regular(s_c);
-    float amax = 0.0f;
-    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && (p.ldc % 16) == 0 &&
-                          ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
-    if (interior) {
-      // codes parked in a [BM][BN + 16] byte tile, then whole rows leave with 16-byte lanes
-      constexpr int CROW8 = BN + 16;
-      uint8_t* Cs = smem;
+    const int rows_in = p.M - m0 < BM ? (int)(p.M - m0) : BM;  // rows / columns of the tile inside C
+    const int cols_in = p.N - n0 < BN ? (int)(p.N - n0) : BN;
+    const bool interior = rows_in == BM && cols_in == BN;
+    // y = acc * fl32(sa * sb) + bias in fp32, in place, and the largest |y|
+    // over the outputs inside C with NaN propagated (v_maximum3): a NaN
+    // result says some output there is NaN
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int lm = wm * WM + 16 * i + r16;
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          *reinterpret_cast<uint32_t*>(Cs + lm * CROW8 + wn * WN + 16 * j + 4 * ng) =
-              quant4<OUT>(acc[i][j], sab, bias_v[j], s_c, sreg, 0xFu, amax);
-      }
-      __syncthreads();
-      constexpr int LPR = BN / 16, RPW = 64 / LPR;
-      const int sub = lane / LPR, cl = lane % LPR;
-#pragma unroll 4
-      for (int rr = wid * RPW + sub; sub < RPW && rr < BM; rr += RPW * NWAVES) {
-        const uint4 v = *reinterpret_cast<const uint4*>(Cs + rr * CROW8 + 16 * cl);
-        *reinterpret_cast<uint4*>(C + (m0 + rr) * p.ldc + n0 + 16 * cl) = v;
-      }
-    } else {
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int64_t gm = m0 + wm * WM + 16 * i + r16;
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(acc[i][j][r], sab, bias_v[j][r]);
+    auto tile_max = [&](auto maxop) {
+      float m = 0.0f;
+      if (interior) {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int64_t gn = n0 + wn * WN + 16 * j + 4 * ng;
-          uint32_t valid = 0;
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) valid |= (uint32_t)(gm < p.M && gn + r < p.N) << r;
-          const uint32_t code = quant4<OUT>(acc[i][j], sab, bias_v[j], s_c, sreg, valid, amax);
-          if (valid == 0) continue;
-          uint8_t* dst = C + gm * p.ldc + gn;
-          if (valid == 0xFu && ((reinterpret_cast<uintptr_t>(dst) & 3u) == 0)) {
-            *reinterpret_cast<uint32_t*>(dst) = code;
-          } else {
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = maxop(m, fabsf(acc[i][j][r]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const bool row_in = wm * WM + 16 * i + r16 < rows_in;
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if ((valid >> r) & 1u) dst[r] = (uint8_t)(code >> (8 * r));
+              if (row_in && wn * WN + 16 * j + 4 * ng + r < cols_in) m = maxop(m, fabsf(acc[i][j][r]));
+        }
+      }
+      return m;
+    };
+    float amax = tile_max([](float a, float b) { return __builtin_elementwise_maximum(a, b); });
+    // Codes go to a [BM][BN + 16] byte tile in LDS (the stages are free after
+    // the K loop), then whole rows leave in 16-byte pieces.  The encoder is
+    // chosen once for the whole wave: the hardware conversion, or the integer
+    // encoder when any lane holds a NaN output (the conversion's NaN code
+    // differs) or the scale is not regular (y * s may be NaN where y is not).
+    constexpr int CROW8 = BN + 16;
+    uint8_t* Cs = smem;
+    const bool fast = !__any(amax != amax) && sreg;
+    // With no lane's fl32(amax |s|) above fmt_max no code needs the clamp:
+    // fl32(|y| |s|) <= fl32(amax |s|) since rounding is monotonic.
+    if (fast && !__any(amax * fabsf(s_c) > FmtTraits<OUT>::kMax)) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const v4f y = acc[i][j];
+          *reinterpret_cast<uint32_t*>(Cs + (wm * WM + 16 * i + r16) * CROW8 + wn * WN + 16 * j + 4 * ng) =
+              cvt4_inrange<OUT>(y[0] * s_c, y[1] * s_c, y[2] * s_c, y[3] * s_c);
+        }
+    } else if (fast) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const v4f y = acc[i][j];
+          *reinterpret_cast<uint32_t*>(Cs + (wm * WM + 16 * i + r16) * CROW8 + wn * WN + 16 * j + 4 * ng) =
+              cvt4<OUT>(y[0] * s_c, y[1] * s_c, y[2] * s_c, y[3] * s_c);
+        }
+    } else {
+      // the amax leaves NaN out (fmaxf returns the other operand for a NaN)
+      amax = tile_max([](float a, float b) { return fmaxf(a, b); });
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const v4f y = acc[i][j];
+          *reinterpret_cast<uint32_t*>(Cs + (wm * WM + 16 * i + r16) * CROW8 + wn * WN + 16 * j + 4 * ng) =
+              enc4_exact<OUT>(y[0] * s_c, y[1] * s_c, y[2] * s_c, y[3] * s_c);
+        }
+    }
+    __syncthreads();
+    {
+      constexpr int LPR = BN / 16, RPW = 64 / LPR;
+      const int sub = lane / LPR, cl = lane % LPR;
+      const bool vec = (p.ldc % 16) == 0 && (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+      if (interior && vec) {
+#pragma unroll 4
+        for (int rr = wid * RPW + sub; sub < RPW && rr < BM; rr += RPW * NWAVES) {
+          const uint4 v = *reinterpret_cast<const uint4*>(Cs + rr * CROW8 + 16 * cl);
+          *reinterpret_cast<uint4*>(C + (m0 + rr) * p.ldc + n0 + 16 * cl) = v;
+        }
+      } else {
+        for (int rr = wid * RPW + sub; sub < RPW && rr < rows_in; rr += RPW * NWAVES) {
+          const uint8_t* src = Cs + rr * CROW8 + 16 * cl;
+          uint8_t* dst = C + (m0 + rr) * p.ldc + n0 + 16 * cl;
+          if (vec && 16 * cl + 16 <= cols_in) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+          } else {
+            for (int b = 0; b < 16 && 16 * cl + b < cols_in; ++b) dst[b] = src[b];
           }
         }
       }
