@@ -14,7 +14,8 @@ of the GPU and no launch waits on Python:
   * each kernel's average launch duration comes from back-to-back launches
     of that kernel over rotating inputs between one event pair (an event
     between every pair of kernels costs ~5 us of GPU time on its own, which
-    would inflate a 10 us kernel by a third).
+    would inflate a 10 us kernel by a third); the kernels take turns in
+    --rounds such windows and each reports its median window.
 
 Prints one JSON line (value = GEMM TFLOP/s at 4096^3).
 """
@@ -50,6 +51,8 @@ def parse():
                     help="also run a plain 512 MiB device copy (counter calibration)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the clock-sampled run of the headline GEMM (counter-collection runs)")
+    ap.add_argument("--rounds", type=int, default=5,
+                    help="timing windows per kernel, interleaved across kernels; the median window counts")
     ap.add_argument("--launches", type=int, default=0,
                     help="back-to-back launches per headline kernel (default max(10, steps))")
     ap.add_argument("--trace-summary", metavar="CSV",
@@ -325,6 +328,10 @@ class ClockSampler:
                "min_MHz": min(self.samples), "max_MHz": max(self.samples)}
         if self.avg_samples:
             out["average_gfxclk_median_MHz"] = statistics.median(self.avg_samples)
+        if max(self.samples) == min(self.samples) and max(self.samples) < 500:
+            # an MFMA-bound GEMM runs the graphics clock near 2 GHz; a reading
+            # that never changes and sits far below is not this run's clock
+            out["suspect"] = "constant reading below 500 MHz under load: the metrics table did not update"
         return out
 
 
@@ -630,22 +637,30 @@ def main():
         "mm_fp8_kmajor": lambda i: fp8mi.fp8_mm(A_km[i % nm].t(), B_km[i % nm].t(), fp8mi.E4M3, fp8mi.E4M3, sa, sb,
                                                 bias, out=C_out),
     }
-    us = []
-    clock = None
-    for nme in names:
-        if nme == "mm_fp8" and not args.no_clock:
-            # sample the graphics clock over a longer run of the headline GEMM
-            with ClockSampler() as cs:
-                timed(launches[nme], 5000)
-            clock = cs.summary()
-        us.append(timed(launches[nme], nlaunch) * 1e3)
     # practical HBM ceiling: the streaming reference kernel moving the same
     # bytes as the row / transposed quantize (read 2 B, write 1 B per element)
     # and as the dual quantize (read 2 B, write 2 B), over the same inputs
     ref_row = torch.empty(R * C, dtype=torch.uint8, device=dev)
     ref_dual = torch.empty(R * C * 2, dtype=torch.uint8, device=dev)
-    ceil_us = {"row": timed(lambda i: fp8mi.stream_reference(xq[i % nq], ref_row), nlaunch) * 1e3,
-               "dual": timed(lambda i: fp8mi.stream_reference(xq[i % nq], ref_dual), nlaunch) * 1e3}
+    launches["stream_row"] = lambda i: fp8mi.stream_reference(xq[i % nq], ref_row)
+    launches["stream_dual"] = lambda i: fp8mi.stream_reference(xq[i % nq], ref_dual)
+    clock = None
+    if not args.no_clock:
+        # sample the graphics clock over a longer run of the headline GEMM
+        with ClockSampler() as cs:
+            timed(launches["mm_fp8"], 5000)
+        clock = cs.summary()
+    # every kernel is timed in `rounds` windows of nlaunch back-to-back
+    # launches, the kernels taking turns window by window (so that no kernel
+    # sees only the chip's state after one particular neighbour); the median
+    # window counts
+    import statistics
+    windows = {nme: [] for nme in launches}
+    for _ in range(args.rounds):
+        for nme in launches:
+            windows[nme].append(timed(launches[nme], nlaunch) * 1e3)
+    us = [statistics.median(windows[nme]) for nme in names]
+    ceil_us = {"row": statistics.median(windows["stream_row"]), "dual": statistics.median(windows["stream_dual"])}
     del ref_row, ref_dual
     qbytes = {"quantize_row": R * C * 3, "quantize_transposed": R * C * 3, "quantize_dual": R * C * 4,
               "quantize_dynamic_row": R * C * 3, "quantize_dynamic_dual": R * C * 4}
@@ -696,6 +711,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(mm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(mm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
                      "kernel": "mm_fp8", "us_per_launch": round(float(us[3]), 3), "launches": nlaunch,
+                     "timing": f"median of {args.rounds} windows of {nlaunch} back-to-back launches, "
+                               "interleaved with the other kernels' windows (HIP events on the launch stream)",
                      "algorithmic_flops": flops},
         "roofline_quantize": {"bound": "hbm", "achieved": quant["quantize_dual"]["GBps"], "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": quant["quantize_dual"]["frac_hbm_peak"], "traffic": None,

@@ -244,10 +244,23 @@ template <int LPW, int MAXR> __device__ __forceinline__ void wait_steps(int r) {
 // stages (DEEP - 1 steps of loads in flight) for the small tiles of
 // problems that leave CUs idle, where each workgroup's chain of load
 // latencies sets the time.
-template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS, int OUT, int LAY, bool PREC,
-          int DEEP = 0>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma(MmArgs p, int64_t tiles_m,
-                                                                                 int64_t tiles_n, int group_m) {
+// LDS of one tile's workgroup, carved from one pool: the load stages (or
+// the staged C tile, whichever is larger), the tile's bias, the reduction
+// words of the quantizing epilogue.
+template <int BM, int BN, int NWAVES, int DEEP> struct TileLds {
+  static constexpr int kStages = DEEP > 0 ? DEEP : (BM * BN <= 64 * 128 ? 3 : 2);
+  static constexpr int kStage = (BM + BN) * kBK;
+  static constexpr int kCTile = BM * (BN + 8) * 2;
+  static constexpr int kSmem = kStages * kStage > kCTile ? kStages * kStage : kCTile;
+  static constexpr int kBias = kSmem;           // BN floats
+  static constexpr int kRed = kBias + 4 * BN;   // NWAVES + 1 words
+  static constexpr int kBytes = kRed + 4 * (NWAVES + 1);
+};
+
+// One BM x BN output tile at (m0, n0) of batch blockIdx.z, with `pool` the
+// workgroup's TileLds bytes.
+template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int OUT, int LAY, bool PREC, int DEEP>
+__device__ __forceinline__ void mm_tile(const MmArgs& p, const int64_t m0, const int64_t n0, uint8_t* pool) {
   constexpr bool KMA = (LAY & 1) != 0, KMB = (LAY & 2) != 0;
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -265,16 +278,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
   constexpr int STAGES = DEEP > 0 ? DEEP : (BM * BN <= 64 * 128 ? 3 : 2);
   static_assert(DEEP == 0 || (DEEP >= 3 && BM * BN <= 64 * 128), "deep pipelines are for the small tiles");
   constexpr int LPW = LA + LB;  // load instructions per wave and K step
-  constexpr int SMEM = STAGES * STAGE > BM * CROW * 2 ? STAGES * STAGE : BM * CROW * 2;
-  __shared__ __align__(16) uint8_t smem[SMEM];
+  using Lds = TileLds<BM, BN, NWAVES, DEEP>;
+  static_assert(Lds::kStages == STAGES && Lds::kStage == STAGE && Lds::kCTile == BM * CROW * 2, "LDS layout");
+  uint8_t* const smem = pool;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int64_t bz = blockIdx.z;
-  int64_t tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int ext_a = (int)(KMA ? p.a_extent_km(m0) : p.a_extent_from(m0));
   const int ext_b = (int)(KMB ? p.b_extent_km(n0) : p.b_extent_from(n0));
   const v4i rsa = buffer_rsrc(p.a + bz * p.stride_a + (KMA ? m0 : m0 * p.lda), ext_a);
@@ -300,7 +311,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
   // latency showed once per tile, and once per element for 16- and 8-bit
   // biases: +4.5 µs (fp32) and +8.5 µs (bf16) at 8192 x 6912 x 1536.)
   static_assert(BN <= 64 * NWAVES, "one bias column per thread");
-  __shared__ __align__(16) float bias_s[BN];
+  float* const bias_s = reinterpret_cast<float*>(pool + Lds::kBias);
   const bool bias_col = p.bias != nullptr && tid < BN && n0 + tid < p.N;
   const uint32_t bias_bits = bias_col ? load_bias_bits(p, n0 + tid) : 0u;
   auto park_bias = [&]() {
@@ -515,7 +526,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
     // Quantizing epilogue.  The output scale comes from the ring (read before
     // this workgroup's amax is published, so before the fold can replace it)
     // or from the caller.
-    __shared__ float red_c[NWAVES + 1];
+    float* const red_c = reinterpret_cast<float*>(pool + Lds::kRed);
     uint8_t* C = static_cast<uint8_t*>(p.c) + bz * p.stride_c;
     const float s_c = p.c_ring ? __uint_as_float(p.c_ring[p.c_H]) : *p.c_scale;
     const bool sreg = scale_regular(s_c);
@@ -685,6 +696,42 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma
   }
 }
 
+template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS, int OUT, int LAY, bool PREC,
+          int DEEP = 0>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma(MmArgs p, int64_t tiles_m,
+                                                                                 int64_t tiles_n, int group_m) {
+  __shared__ __align__(16) uint8_t pool[TileLds<BM, BN, WAVES_M * WAVES_N, DEEP>::kBytes];
+  int64_t tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+  mm_tile<FA, FB, BM, BN, WAVES_M, WAVES_N, OUT, LAY, PREC, DEEP>(p, tm * BM, tn * BN, pool);
+}
+
+// Mixed grid for a last round of 256 x 256 tiles that would leave most CUs
+// idle: workgroups 0 .. tiles_m * tiles_n - 1 take the 256 x 256 tiles of
+// columns [0, n_band), dispatched first; the rest take 128 x 256 tiles of
+// the band [n_band, N), which start as CUs come free and take about half a
+// big tile's time.  Both shapes sum every output's K in the same MFMA
+// order, so the result equals the all-256 x 256 launch bit for bit.
+template <int FA, int FB, int OUT, int LAY>
+__global__ void __launch_bounds__(512, 1) mm_fp8_mixed(MmArgs p, int64_t tiles_m, int64_t tiles_n,
+                                                       int64_t band_tiles_m, int64_t band_tiles_n, int64_t n_band,
+                                                       int group_m) {
+  using Big = TileLds<256, 256, 8, 0>;
+  using Band = TileLds<128, 256, 8, 0>;
+  __shared__ __align__(16) uint8_t pool[Big::kBytes > Band::kBytes ? Big::kBytes : Band::kBytes];
+  const int64_t nbig = tiles_m * tiles_n;
+  int64_t tm, tn;
+  if ((int64_t)blockIdx.x < nbig) {
+    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    mm_tile<FA, FB, 256, 256, 2, 4, OUT, LAY, false, 0>(p, tm * 256, tn * 256, pool);
+  } else {
+    // nbig is a multiple of 8, so the band's own index keeps the XCD of blockIdx.x
+    tile_coords((int64_t)blockIdx.x - nbig, band_tiles_m, band_tiles_n, group_m, tm, tn);
+    mm_tile<FA, FB, 128, 256, 2, 4, OUT, LAY, false, 0>(p, tm * 128, n_band + tn * 256, pool);
+  }
+}
+
+
 // Tile dispatch (measured on MI355X over the shapes of the test configs):
 // the 8-wave big-tile kernels whenever their tiles (x batch) cover at least
 // 60% of the CUs -- one round of big tiles beats several rounds of small ones
@@ -708,8 +755,37 @@ static hipError_t launch_dma(const MmArgs& p, hipStream_t st) {
 
 // FP8MI_MM_TILE: a forced tile for tuning (-1 when unset or invalid).
 static inline int mm_forced_tile() {
-  static const int forced = env_int_in("FP8MI_MM_TILE", 0, 6, -1);
+  static const int forced = env_int_in("FP8MI_MM_TILE", 0, 7, -1);
   return forced == 4 ? -1 : forced;
+}
+
+// Columns of 256 x 256 tiles handed to the 128 x 256 band of mm_fp8_mixed,
+// or 0 when the mixed grid does not apply: one batch, at least two rounds
+// of 256 x 256 tiles with the last at most half full, the band the last
+// ceil(last / tiles_m) tile columns, the big tiles left a multiple of 8 and
+// the band's 128 x 256 tiles at most one per CU.  (8192 x 6912 x 1536: 864
+// tiles on 256 CUs = 3 rounds + 96 -> 768 big tiles + a 8192 x 768 band of
+// 192 tiles.)
+static inline int64_t mixed_band_cols(const MmArgs& p, int ncu) {
+  if (p.batch != 1) return 0;
+  const int64_t tm = (p.M + 255) / 256, tn = (p.N + 255) / 256, t = tm * tn;
+  const int64_t rounds = (t + ncu - 1) / ncu;
+  if (rounds < 2) return 0;
+  const int64_t last = t - (rounds - 1) * ncu;
+  if (2 * last > ncu) return 0;
+  const int64_t cb = (last + tm - 1) / tm;
+  if (cb >= tn || (tm * (tn - cb)) % 8 != 0) return 0;
+  return ((p.M + 127) / 128) * cb <= ncu ? cb : 0;
+}
+
+template <int FA, int FB, int OUT, int LAY> static hipError_t launch_mixed(const MmArgs& p, int64_t cb,
+                                                                            hipStream_t st) {
+  const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256 - cb;
+  const int64_t band_m = (p.M + 127) / 128;
+  const dim3 grid((unsigned)(tiles_m * tiles_n + band_m * cb), 1, 1);
+  hipLaunchKernelGGL((mm_fp8_mixed<FA, FB, OUT, LAY>), grid, dim3(512), 0, st, p, tiles_m, tiles_n, band_m, cb,
+                     tiles_n * 256, 4);
+  return hipGetLastError();
 }
 
 static inline int pick_tile(const MmArgs& p, int ncu) {
@@ -737,7 +813,8 @@ static inline int pick_tile(const MmArgs& p, int ncu) {
   // linear), 256 x 256 when it saves a round (8192 x 6912 x 1536: 4 rounds
   // instead of 5, 3% faster).
   const int64_t cost256 = ((t256 + ncu - 1) / ncu) * 256, cost192 = ((t192 + ncu - 1) / ncu) * 230;
-  return cost192 < cost256 ? 3 : 0;
+  if (cost192 < cost256) return 3;
+  return mixed_band_cols(p, ncu) > 0 ? 7 : 0;
 }
 
 
@@ -748,16 +825,20 @@ template <int FA, int FB, int OUT, int LAY> static hipError_t launch_tile(const 
     case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2, OUT, LAY>(p, st);
     case 5: return launch_dma<FA, FB, 64, 64, 1, 4, 2, OUT, LAY>(p, st);
     case 6: return launch_dma<FA, FB, 64, 64, 1, 4, 1, OUT, LAY, false, 8>(p, st);
+    case 7: {
+      const int64_t cb = mixed_band_cols(p, device_cu_count());
+      if (cb > 0) return launch_mixed<FA, FB, OUT, LAY>(p, cb, st);
+      return launch_dma<FA, FB, 256, 256, 2, 4, 1, OUT, LAY>(p, st);
+    }
     default: return launch_dma<FA, FB, 64, 128, 1, 4, 2, OUT, LAY>(p, st);
   }
 }
 
 // The big-tile family for one format pair, output type and layout (operand
-// extents below 2^31 bytes).  A last round of big tiles that leaves CUs idle
-// is kept: splitting the columns it covers into a second, small-tile launch
-// measured slower (8192 x 6912 x 1536: 98.4 us split, 94.4 us as four rounds
-// of 256 x 256 -- the partial fourth round takes ~18 us against ~25 us for a
-// full one, and the 8192 x 768 remainder 15.9-17.5 us plus a launch).
+// extents below 2^31 bytes).  A mostly idle last round of 256 x 256 tiles
+// becomes the 128 x 256 band of mm_fp8_mixed, in the same launch (as a
+// second, small-tile launch it measured slower: 8192 x 6912 x 1536 98.4 us
+// against 94.4 us for four rounds of 256 x 256).
 template <int FA, int FB, int OUT, int LAY = 0> static hipError_t launch_dma_family(const MmArgs& p, hipStream_t st) {
   return launch_tile<FA, FB, OUT, LAY>(p, pick_tile(p, device_cu_count()), st);
 }
