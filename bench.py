@@ -201,7 +201,7 @@ TRAFFIC_KERNELS = {
     ("amax_partials<2>", 196864): "amax_pass_8192x1536",
     ("stream_kernel<true>", 393216): "stream_reference_row_bytes",
     ("stream_kernel<false>", 393216): "stream_reference_dual_bytes",
-    ("mm_fp8_dma<0, 0, 256, 256, 2, 4, 1, -1, 0, false, 0>", 442368): "training_forward_8192x6912x1536",
+    ("mm_fp8_mixed<0, 0, -1, 0>", 491520): "training_forward_8192x6912x1536",
     ("mm_fp8_dma<1, 0, 256, 192, 2, 4, 1, -1, 0, false, 0>", 131072): "training_dx_8192x1536x6912",
     ("mm_fp8_dma<1, 0, 256, 192, 2, 4, 1, -1, 0, false, 0>", 110592): "training_dw_6912x1536x8192",
     ("quantize_tiled_pf<2, 1, 2, true, false>", 196608): "training_dy_dual_bias_grad_8192x6912",
@@ -292,16 +292,17 @@ class ClockSampler:
                 h = amdsmi.amdsmi_get_processor_handles()[0]
                 self._ready.set()
                 while not self._stop.is_set():
-                    # the SMU's gpu-metrics table: one current graphics clock per XCD (MHz)
+                    # the driver's current graphics DPM level: its list holds the
+                    # measured frequency at index `current` (Hz).  The SMU's
+                    # gpu-metrics table, the other source, went stale on some hosts.
+                    f = amdsmi.amdsmi_get_clk_freq(h, amdsmi.AmdSmiClkType.GFX)
+                    cur, freqs = f.get("current"), f.get("frequency") or []
+                    if isinstance(cur, int) and 0 <= cur < len(freqs) and freqs[cur]:
+                        self.samples.append(freqs[cur] / 1e6)
                     m = amdsmi.amdsmi_get_gpu_metrics_info(h)
                     clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
-                    if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
-                        clks = [m["current_gfxclk"]]
                     if clks:
-                        self.samples.append(sum(clks) / len(clks))
-                    avg = m.get("average_gfxclk_frequency")
-                    if isinstance(avg, (int, float)) and avg > 0:
-                        self.avg_samples.append(float(avg))
+                        self.avg_samples.append(sum(clks) / len(clks))
                     time.sleep(self.period)
             finally:
                 amdsmi.amdsmi_shut_down()
@@ -321,17 +322,17 @@ class ClockSampler:
 
     def summary(self):
         import statistics
-        src = "amdsmi gpu metrics: current_gfxclks (mean over XCDs), average_gfxclk_frequency"
+        src = "amdsmi_get_clk_freq(GFX): frequency of the current DPM level, sampled every 5 ms"
         if not self.samples:
             return {"source": src, "error": self.error or "no samples"}
         out = {"source": src, "samples": len(self.samples), "median_MHz": statistics.median(self.samples),
                "min_MHz": min(self.samples), "max_MHz": max(self.samples)}
         if self.avg_samples:
-            out["average_gfxclk_median_MHz"] = statistics.median(self.avg_samples)
-        if max(self.samples) == min(self.samples) and max(self.samples) < 500:
-            # an MFMA-bound GEMM runs the graphics clock near 2 GHz; a reading
-            # that never changes and sits far below is not this run's clock
-            out["suspect"] = "constant reading below 500 MHz under load: the metrics table did not update"
+            # the gpu-metrics table's per-XCD clocks, for comparison: a value
+            # that never changes under load is a stale table, not the clock
+            out["gpu_metrics_current_gfxclks_median_MHz"] = statistics.median(self.avg_samples)
+            if max(self.avg_samples) == min(self.avg_samples):
+                out["gpu_metrics_note"] = "constant over the run: stale table"
         return out
 
 
