@@ -51,6 +51,7 @@ struct MmArgs {
   float* c_scale_inv_out = nullptr;
   float* c_amax_out = nullptr;
   int layout = 0;                     // bit 0: A is [K, M] (K-major), bit 1: B is [K, N]
+  int early_loads = 0;                // set by the launch: big tiles issue a K step's loads early
 
   // Bytes of one batch's A (B) from row r on: the last row ends at K.
   __host__ __device__ int64_t a_extent_from(int64_t r) const { return r < M ? (M - 1 - r) * lda + K : 0; }
