@@ -226,7 +226,12 @@ __device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t
   const bool nan = am.has_nan();
   const float camax = nan ? nan_free_absmax<kFlatElemsPerThread>(f) : am.value();
   uint32_t code[kFlatElemsPerThread / 4];
-  if (!nan && sreg) {
+  if (!nan && sreg && camax * fabsf(s) <= FmtTraits<FMT>::kMax) {
+    // no clamp needed: fl32(|x| |s|) <= fl32(camax |s|) (monotonic rounding)
+#pragma unroll
+    for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
+      code[q] = cvt4_inrange<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
+  } else if (!nan && sreg) {
 #pragma unroll
     for (int q = 0; q < kFlatElemsPerThread / 4; ++q)
       code[q] = cvt4<FMT>(f[4 * q] * s, f[4 * q + 1] * s, f[4 * q + 2] * s, f[4 * q + 3] * s);
@@ -444,7 +449,15 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
     }
     amax = fmaxf(amax, camax);
     uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
-    if (!nan && sreg) {
+    if (!nan && sreg && camax * fabsf(s) <= FmtTraits<FMT>::kMax) {
+      // no clamp needed: fl32(|x| |s|) <= fl32(camax |s|) (monotonic rounding)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          rw[i][h] = cvt4_inrange<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
+                                       f[i][4 * h + 3] * s);
+    } else if (!nan && sreg) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -629,7 +642,15 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
     }
     amax = fmaxf(amax, camax);
     uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
-    if (!nan && sreg) {
+    if (!nan && sreg && camax * fabsf(s) <= FmtTraits<FMT>::kMax) {
+      // no clamp needed: fl32(|x| |s|) <= fl32(camax |s|) (monotonic rounding)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          rw[i][h] = cvt4_inrange<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
+                                       f[i][4 * h + 3] * s);
+    } else if (!nan && sreg) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
