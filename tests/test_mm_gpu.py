@@ -383,3 +383,27 @@ def test_training_forward_shape_exact(layout, bias_dtype):
     got = np_bf16_bits(y)[:512, 6100:6200]
     ref, _ = O.mm(a[:512], O.E4M3, b[6100:6200], O.E4M3, sa, sb, bias_v[6100:6200].astype(np.float64))
     assert np.array_equal(got, ref[0])
+
+
+def test_mixed_grid_ragged_exact():
+    """8000 x 6900 x 1536: the same 864-tile count as the training forward,
+    so the launch is the mixed grid (768 tiles of 256 x 256 over columns
+    0..6143, then a band of 128 x 256 tiles over 6144..6899), with ragged
+    edges in both: the last big-tile row holds 64 rows, the last band tile
+    244 columns.  Exact small-integer data: sampled rows, the last 64 rows,
+    and every column around the big / band boundary and the right edge,
+    bit-exact against the oracle."""
+    M, N, K = 8000, 6900, 1536
+    a = make_int_codes((M, K), O.E4M3, 83, 0, 0)
+    b = make_int_codes((N, K), O.E4M3, 83, 0, 1)
+    bias_v = synth.rng(83, 0, 2).integers(-256, 257, size=N).astype(np.float32)
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    y = fp8mi.fp8_mm(to_dev_codes(a), to_dev_codes(b), 0, 0, scalar(sa), scalar(sb),
+                     torch.from_numpy(bias_v).to(DEV))
+    yb = np_bf16_bits(y)
+    rows = np.unique(np.concatenate([sample_rows(M, 48, 83, 0, 3), np.arange(M - 64, M)]))
+    check(yb, a, O.E4M3, b, O.E4M3, sa, sb, bias_v.astype(np.float64), rows, tag="mixed ragged", exact=True)
+    for c0, c1 in ((6080, 6210), (6600, 6900)):
+        for r0, r1 in ((0, 256), (M - 320, M)):
+            ref, _ = O.mm(a[r0:r1], O.E4M3, b[c0:c1], O.E4M3, sa, sb, bias_v[c0:c1].astype(np.float64))
+            assert np.array_equal(yb[r0:r1, c0:c1], ref[0]), (r0, c0)
