@@ -14,8 +14,9 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["abi.hip", "quantize.hip", "mm_fp8.hip", "mm_fp8_q8.hip", "mm_fp8_km.hip", "mm_fp8_prec.hip",
-           "mm_fp8_prec_km.hip", "mm_fp8_prec_q8.hip", "grad_bias.hip", "stream.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "mm_fp8.hip", "mm_fp8_q8.hip", "mm_fp8_km.hip", "mm_fp8_km_q8_a.hip",
+           "mm_fp8_km_q8_b.hip", "mm_fp8_km_q8_ab.hip", "mm_fp8_prec.hip", "mm_fp8_prec_km.hip", "mm_fp8_prec_q8.hip",
+           "mm_fp8_prec_km_q8.hip", "grad_bias.hip", "stream.hip"]
 LIB = os.path.join(PKG, "libfp8mi.so")
 
 HIPCC_FLAGS = [

@@ -314,7 +314,6 @@ fp8mi_status fp8_mm_ex(const uint8_t* a, int fmt_a, int64_t lda, int64_t stride_
   } else if (c_scale || c_ring || c_scale_inv_out || c_amax_out) {
     return fail(FP8MI_ERR_ARG, "output scale, ring, scale_inv and amax are for an fp8 output only");
   }
-  if (fp8_out && layout != 0) return fail(FP8MI_ERR_UNSUPPORTED, "K-major operands take a bf16 output");
   if (M < 0 || N < 0 || K < 0 || batch < 0)
     return fail(FP8MI_ERR_SHAPE, "negative size M=%lld N=%lld K=%lld batch=%lld", (long long)M, (long long)N,
                 (long long)K, (long long)batch);

@@ -65,15 +65,22 @@ struct MmArgs {
 };
 
 hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
-// fp8-output GEMM (p.out_fmt >= 0, operand extents below 2^31 bytes).
+// fp8-output GEMM (p.out_fmt >= 0, either layout, operand extents below 2^31 bytes).
 hipError_t launch_mm_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 // bf16-output GEMM with K-major operand(s) (p.layout != 0, extents below 2^31 bytes).
 hipError_t launch_mm_km(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+// fp8-output GEMM with K-major operand(s), one per layout tag (1: A, 2: B,
+// 3: both), called by launch_mm_q8.
+hipError_t launch_mm_km_q8_l1(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+hipError_t launch_mm_km_q8_l2(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+hipError_t launch_mm_km_q8_l3(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 // Short K (K <= kPreciseMaxK, mm_fp8_kernel.h): the precise-accumulation
-// kernels, bf16 NT / bf16 K-major / fp8 output (operand extents below 2^31 bytes).
+// kernels, bf16 NT / bf16 K-major / fp8 output NT / fp8 output K-major
+// (operand extents below 2^31 bytes).
 hipError_t launch_mm_prec_nt(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 hipError_t launch_mm_prec_km(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 hipError_t launch_mm_prec_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
+hipError_t launch_mm_prec_km_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st);
 // One fp32 word set to 0 on the stream (a fill kernel, capturable).
 hipError_t launch_zero_word(float* p, hipStream_t st);
 

@@ -150,8 +150,8 @@ template <int FA, int FB> static hipError_t launch_fmts(const MmArgs& p, hipStre
 }
 
 hipError_t launch_mm(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st) {
-  if (p.layout != 0) return launch_mm_km(p, fmt_a, fmt_b, st);
   if (p.out_fmt >= 0) return launch_mm_q8(p, fmt_a, fmt_b, st);
+  if (p.layout != 0) return launch_mm_km(p, fmt_a, fmt_b, st);
   if (fmt_a == kE4M3 && fmt_b == kE4M3) return launch_fmts<kE4M3, kE4M3>(p, st);
   if (fmt_a == kE5M2 && fmt_b == kE4M3) return launch_fmts<kE5M2, kE4M3>(p, st);
   if (fmt_a == kE4M3 && fmt_b == kE5M2) return launch_fmts<kE4M3, kE5M2>(p, st);

@@ -4,7 +4,8 @@
 // transposed operands into the GEMM).  The mm_fp8_dma kernels load such a
 // tile into LDS as k-rows (LDS-DMA, swizzled 16-byte chunks) and build the
 // MFMA operand fragments with gfx950's LDS transpose read (ds_read_b64_tr_b8).
-// bf16 output; the same tile family and dispatch as the NT GEMM (64 x 64 included).
+// bf16 output (fp8 output: mm_fp8_km_q8.h); the same tile family and
+// dispatch as the NT GEMM (64 x 64 included).
 #include "mm_fp8_kernel.h"
 
 namespace fp8mi {

@@ -44,6 +44,12 @@ hipError_t launch_mm_q8(const MmArgs& p, int fmt_a, int fmt_b, hipStream_t st) {
     const hipError_t e = launch_zero_word(p.c_amax_out, st);
     if (e != hipSuccess) return e;
   }
+  if (p.layout != 0) {
+    if (mm_precise(p)) return launch_mm_prec_km_q8(p, fmt_a, fmt_b, st);
+    if (p.layout == 1) return launch_mm_km_q8_l1(p, fmt_a, fmt_b, st);
+    if (p.layout == 2) return launch_mm_km_q8_l2(p, fmt_a, fmt_b, st);
+    return launch_mm_km_q8_l3(p, fmt_a, fmt_b, st);
+  }
   if (mm_precise(p)) return launch_mm_prec_q8(p, fmt_a, fmt_b, st);
   if (fmt_a == kE4M3 && fmt_b == kE4M3) return launch_out<kE4M3, kE4M3>(p, st);
   if (fmt_a == kE5M2 && fmt_b == kE4M3) return launch_out<kE5M2, kE4M3>(p, st);

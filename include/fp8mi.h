@@ -231,9 +231,10 @@ FP8MI_API fp8mi_status fp8_mm(const uint8_t* a, int fmt_a, int64_t lda, int64_t 
  *              3-D operands into the GEMM).  A K-major A is a [K, lda] array
  *              of K full rows (K * lda readable bytes per batch, the last
  *              row's padding included) with lda >= M (B: [K, ldb], ldb >= N),
- *              lda % 16 == 0, extents below 2^31 bytes and a bf16 output
- *              (else FP8MI_ERR_UNSUPPORTED); the result is that of the same
- *              operands in NT form, bit for bit.
+ *              lda % 16 == 0 and extents below 2^31 bytes (else
+ *              FP8MI_ERR_UNSUPPORTED), with either output type; the result
+ *              (bf16 values, or fp8 codes, amax and ring words) is that of the
+ *              same operands in NT form, bit for bit.
  * Other arguments and requirements as fp8_mm.  M, N or batch 0 writes no
  * codes; an fp8 output then still folds amax 0 into its ring (or writes
  * 1 / s_c and amax 0).  y is fp32, so its accumulation error is that of

@@ -354,7 +354,9 @@ def test_mm_ex_rejects(L):
     # layout tags
     assert call(lay=4) == ENUM
     assert call(lay=-1) == ENUM
-    assert call(lay=1, cdt=3, cscale=FAKE) == UNSUP   # K-major operands take a bf16 output
+    # an fp8 output takes K-major operands under the same rules as bf16
+    assert call(lay=1, cdt=3, cscale=FAKE, M=64, lda=48) == SHAPE
+    assert call(lay=1, cdt=3, cscale=FAKE, M=64, lda=72) == UNSUP
     assert call(lay=1, M=64, lda=48) == SHAPE         # K-major A: lda must cover M
     assert call(lay=2, N=64, ldb=48) == SHAPE
     assert call(lay=1, M=64, lda=72) == UNSUP         # lda % 16

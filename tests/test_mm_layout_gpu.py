@@ -1,8 +1,10 @@
 """Layout tags in the GEMM: operands given K-major (transposed views of
 [K, M] / [K, N] storage) are read without a transposed copy through
 ds_read_b64_tr_b8 fragments.  The MFMA sees the same fragments as in NT
-form, so every result must equal the NT result of the same codes bit for bit;
-on exact small-integer data it must also equal the oracle bit for bit."""
+form, so every result must equal the NT result of the same codes bit for bit
+(bf16 values, or fp8 codes, amax and ring words with the quantizing
+epilogue); on exact small-integer data it must also equal the oracle bit for
+bit."""
 import numpy as np
 import pytest
 import torch
@@ -88,8 +90,38 @@ def test_backward_without_transposed_codes():
     check(np_bf16_bits(dx), g, O.E5M2, np.ascontiguousarray(w.T), O.E4M3, 1 / 512, 1 / 64, None, rows, tag="dX")
 
 
-def test_layout_rejects_fp8_output():
-    a = torch.zeros((64, 32), dtype=torch.uint8, device=DEV)
-    b = torch.zeros((32, 64), dtype=torch.uint8, device=DEV)
-    with pytest.raises(fp8mi.Fp8Error):
-        fp8mi.fp8_mm_ex(a, b.t(), 0, 0, out_fmt=0, out_scale=scalar(1.0))
+FP8_OUT_CASES = [((64, 256, 256, 1), "AB"), ((130, 257, 272, 1), "A"), ((130, 257, 272, 1), "B"),
+                 ((1000, 1537, 2048, 1), "AB"), ((256, 384, 640, 3), "A"), ((17, 33, 48, 2), "B"),
+                 ((8000, 6900, 1536, 1), "A")]
+
+
+@pytest.mark.parametrize("case", FP8_OUT_CASES, ids=lambda c: "x".join(map(str, c[0])) + "-" + c[1])
+@pytest.mark.parametrize("fmt_c", [O.E4M3, O.E5M2], ids=["e4m3", "e5m2"])
+def test_layout_fp8_output_equals_nt(case, fmt_c):
+    """K-major operands with the quantizing epilogue: codes, 1/s, amax and the
+    output ring's words equal those of the NT call on the same codes, bit for
+    bit -- with the output's ring (a fresh ring per call, folded once) and with
+    an explicit scale (K = 256 takes the precise accumulation; 8000 x 6900 x
+    1536 the mixed grid)."""
+    (M, N, K, batch), layout = case
+    a = make_codes((batch, M, K), O.E4M3, 53, M, K, 0)
+    b = make_codes((batch, N, K), O.E5M2, 53, M, K, 1)
+    bias = torch.from_numpy(synth.rng(53, M, 2).standard_normal(N).astype(np.float32)).to(DEV)
+    sa, sb = scalar(0.03125), scalar(0.5)
+    A = km_view(a, pad=16) if "A" in layout else to_dev_codes(a)
+    B = km_view(b, pad=32) if "B" in layout else to_dev_codes(b)
+    outs = []
+    for x, y in ((A, B), (to_dev_codes(a), to_dev_codes(b))):
+        ring = fp8mi.new_ring(16, 1.0, DEV)
+        sinv_r, amax_r = torch.zeros(1, device=DEV), torch.zeros(1, device=DEV)
+        q_r = fp8mi.fp8_mm_ex(x, y, 0, 1, sa, sb, bias, out_fmt=FID[fmt_c], out_ring=ring, out_scale_inv=sinv_r,
+                              out_amax=amax_r)
+        sinv_s, amax_s = torch.zeros(1, device=DEV), torch.zeros(1, device=DEV)
+        q_s = fp8mi.fp8_mm_ex(x, y, 0, 1, sa, sb, bias, out_fmt=FID[fmt_c], out_scale=scalar(0.75),
+                              out_scale_inv=sinv_s, out_amax=amax_s)
+        torch.cuda.synchronize()
+        outs.append([q_r.cpu(), ring.cpu(), sinv_r.cpu(), amax_r.cpu(), q_s.cpu(), sinv_s.cpu(), amax_s.cpu()])
+    names = ["codes (ring)", "ring words", "1/s (ring)", "amax (ring)", "codes (scale)", "1/s (scale)", "amax (scale)"]
+    for name, km, nt in zip(names, outs[0], outs[1]):
+        assert torch.equal(km.contiguous().view(torch.uint8), nt.contiguous().view(torch.uint8)), name
+    assert float(outs[1][3]) > 0 and float(outs[1][6]) > 0

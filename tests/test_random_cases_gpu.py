@@ -155,8 +155,8 @@ def test_random_gemm(i):
 
 @pytest.mark.parametrize("i", range(60))
 def test_random_gemm_fp8_out(i):
-    """The quantizing epilogue on random cases: NT operands (as above, no
-    K-major: an fp8 output takes NT operands), E4M3 / E5M2 output codes with an
+    """The quantizing epilogue on random cases: operands as above (K-major
+    with probability 1/3 each), E4M3 / E5M2 output codes with an
     explicit scale or a ring holding a random history, no / bf16 / fp8 bias
     (E4M3 / E5M2 codes with a power-of-two bias scale).  Small-integer data and
     power-of-two scales: codes, amax, scale_inv and ring words bit-exact."""
@@ -195,8 +195,8 @@ def test_random_gemm_fp8_out(i):
                              bias_v, scale=s_c)
         scale_t = scalar(s_c)
     sinv, amax = scalar(-1), scalar(-1)
-    out = fp8mi.fp8_mm_ex(operand(a, False, c["pad_a"]) if batch > 1 else operand(a, False, c["pad_a"])[0],
-                          operand(b, False, c["pad_b"]) if batch > 1 else operand(b, False, c["pad_b"])[0],
+    out = fp8mi.fp8_mm_ex(operand(a, c["a_km"], c["pad_a"]) if batch > 1 else operand(a, c["a_km"], c["pad_a"])[0],
+                          operand(b, c["b_km"], c["pad_b"]) if batch > 1 else operand(b, c["b_km"], c["pad_b"])[0],
                           FID[c["fa"]], FID[c["fb"]], scalar(sa), scalar(sb), bias_t, bias_fmt, bias_scale,
                           out_fmt=FID[fmt_c], out_scale=scale_t, out_ring=ring, out_scale_inv=sinv, out_amax=amax)
     torch.cuda.synchronize()
