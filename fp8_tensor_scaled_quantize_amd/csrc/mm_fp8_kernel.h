@@ -759,7 +759,8 @@ __global__ void __launch_bounds__(512, 1) mm_fp8_mixed(MmArgs p, int64_t tiles_m
 // needs less time per CU (the backward GEMMs of the 1536-wide linear get 256
 // and 216 workgroups instead of 192 and 162, 10-11% faster), and the 64x128 /
 // 4-wave kernel (two per CU, three LDS stages) below 60% -- or 64x64 when the
-// 64x128 tiles number at most one per CU.
+// 64x128 tiles number at most one per CU, and 64x32 (deep pipeline) when
+// even the 64x64 tiles would fill at most half the CUs and K is long.
 // 128x128 is reachable through FP8MI_MM_TILE=1 for tuning.  The first 128x128
 // kernel remains for operands whose byte extent does not fit a 32-bit buffer
 // offset.
@@ -777,7 +778,7 @@ static hipError_t launch_dma(const MmArgs& p0, hipStream_t st) {
 
 // FP8MI_MM_TILE: a forced tile for tuning (-1 when unset or invalid).
 static inline int mm_forced_tile() {
-  static const int forced = env_int_in("FP8MI_MM_TILE", 0, 7, -1);
+  static const int forced = env_int_in("FP8MI_MM_TILE", 0, 8, -1);
   return forced == 4 ? -1 : forced;
 }
 
@@ -827,6 +828,11 @@ static inline int pick_tile(const MmArgs& p, int ncu) {
     const int64_t t128 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
     const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch;
     const bool long_k = p.K >= 6 * kBK;
+    // with even the 64 x 64 tiles at most half a workgroup per CU and a long
+    // K, 64 x 32 tiles (deep pipeline): twice the workgroups, each streaming
+    // half the B panel (best of three runs, one box: 64x8192x2048 8.1 -> 7.5
+    // us, 128x4096x4096 12.1 -> 10.3 us, 64x1536x6912 17.6 -> 14.5 us)
+    if (long_k && 2 * t64 <= (int64_t)ncu) return 8;
     if (t128 <= (int64_t)ncu) return long_k && t64 <= (int64_t)ncu ? 6 : 5;
     return 2;
   }
@@ -849,6 +855,7 @@ template <int FA, int FB, int OUT, int LAY> static hipError_t launch_tile(const 
     case 1: return launch_dma<FA, FB, 128, 128, 2, 2, 2, OUT, LAY>(p, st);
     case 5: return launch_dma<FA, FB, 64, 64, 1, 4, 2, OUT, LAY>(p, st);
     case 6: return launch_dma<FA, FB, 64, 64, 1, 4, 1, OUT, LAY, false, 8>(p, st);
+    case 8: return launch_dma<FA, FB, 64, 32, 4, 1, 1, OUT, LAY, false, 8>(p, st);
     case 7: {
       const int64_t cb = mixed_band_cols(p, device_cu_count());
       if (cb > 0) return launch_mixed<FA, FB, OUT, LAY>(p, cb, st);

@@ -32,7 +32,7 @@ def km_view(codes: np.ndarray, pad: int = 0) -> torch.Tensor:
 
 
 SHAPES = [(64, 256, 256, 1), (130, 257, 272, 1), (1000, 1537, 2048, 1), (2048, 1536, 1536, 1),
-          (256, 384, 640, 3), (17, 33, 48, 2)]
+          (256, 384, 640, 3), (17, 33, 48, 2), (64, 4096, 1024, 1)]   # the last: 64 x 32 tiles
 
 
 @pytest.mark.parametrize("layout", ["A", "B", "AB"])
@@ -91,6 +91,7 @@ def test_backward_without_transposed_codes():
 
 
 FP8_OUT_CASES = [((64, 256, 256, 1), "AB"), ((130, 257, 272, 1), "A"), ((130, 257, 272, 1), "B"),
+                 ((64, 4096, 1024, 1), "AB"),
                  ((1000, 1537, 2048, 1), "AB"), ((256, 384, 640, 3), "A"), ((17, 33, 48, 2), "B"),
                  ((8000, 6900, 1536, 1), "A")]
 
