@@ -396,80 +396,123 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
   const char* xb = static_cast<const char*>(p.x);
   const int64_t t_first = (int64_t)blockIdx.x * tiles_per_block;
   const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
+  const bool x_rows16 = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 && ((p.ld_x * EB) & 15) == 0;
   for (int64_t tile = t_first; tile < t_last; ++tile) {
     int64_t r0, c0;
     tile_origin(tile, tiles_c, ntiles, r0, c0);
     const int64_t cc = c0 + 8 * cg;  // this thread's first column
-    float f[4][8];
-    AbsMax<DT> am;
-    bool all_full = true;
+    uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
+    float f[4][8];      // the values (general path; the bias gradient reads them)
+    if (MODE == kTrans && x_rows16 && r0 + kTileR <= p.rows && c0 + kTileC <= p.cols) {
+      // transposed output, tile inside the tensor, rows on 16 bytes: the four
+      // rows' loads go out back to back, then each row is encoded on its own
+      // (its own NaN and in-range tests, which give the same codes as the
+      // tile-wide tests), so one row's values are live at a time
+      constexpr int NLD = EB == 4 ? 2 : 1;
+      uint4 raw[4][NLD];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = r0 + 4 * rg + i;
-      const char* src = xb + (r * p.ld_x + cc) * EB;
-      const bool full = r < p.rows && cc + 8 <= p.cols;  // vector loads, realigned if the row start is not
-      all_full &= full;
-      if (full) {
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < NLD; ++c)
+          raw[i][c] = reinterpret_cast<const uint4*>(xb + ((r0 + 4 * rg + i) * p.ld_x + cc) * EB)[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        AbsMax<DT> ami;
+        float fr[8];
+#pragma unroll
+        for (int c = 0; c < NLD; ++c) ami.add(raw[i][c]);
         if constexpr (DT == kF32) {
-          uint4 ab[2];
-          load16_any<2>(src, ab);
-          const uint4 a = ab[0], b = ab[1];
-          am.add(a);
-          am.add(b);
-          f[i][0] = __uint_as_float(a.x); f[i][1] = __uint_as_float(a.y);
-          f[i][2] = __uint_as_float(a.z); f[i][3] = __uint_as_float(a.w);
-          f[i][4] = __uint_as_float(b.x); f[i][5] = __uint_as_float(b.y);
-          f[i][6] = __uint_as_float(b.z); f[i][7] = __uint_as_float(b.w);
+          const uint4 lo = raw[i][0], hi = raw[i][NLD - 1];
+          fr[0] = __uint_as_float(lo.x); fr[1] = __uint_as_float(lo.y); fr[2] = __uint_as_float(lo.z);
+          fr[3] = __uint_as_float(lo.w); fr[4] = __uint_as_float(hi.x); fr[5] = __uint_as_float(hi.y);
+          fr[6] = __uint_as_float(hi.z); fr[7] = __uint_as_float(hi.w);
         } else {
-          uint4 a1[1];
-          load16_any<1>(src, a1);
-          const uint4 a = a1[0];
-          am.add(a);
-          widen2<DT>(a.x, f[i][0], f[i][1]); widen2<DT>(a.y, f[i][2], f[i][3]);
-          widen2<DT>(a.z, f[i][4], f[i][5]); widen2<DT>(a.w, f[i][6], f[i][7]);
+          const uint4 v = raw[i][0];
+          widen2<DT>(v.x, fr[0], fr[1]); widen2<DT>(v.y, fr[2], fr[3]);
+          widen2<DT>(v.z, fr[4], fr[5]); widen2<DT>(v.w, fr[6], fr[7]);
         }
+        const bool rnan = ami.has_nan();
+        const float rmax = rnan ? nan_free_absmax<8>(fr) : ami.value();
+        amax = fmaxf(amax, rmax);
+        const bool inrange = !rnan && sreg && rmax * fabsf(s) <= FmtTraits<FMT>::kMax;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float q0 = fr[4 * h] * s, q1 = fr[4 * h + 1] * s, q2 = fr[4 * h + 2] * s, q3 = fr[4 * h + 3] * s;
+          if (inrange) rw[i][h] = cvt4_inrange<FMT>(q0, q1, q2, q3);
+          else if (!rnan && sreg) rw[i][h] = cvt4<FMT>(q0, q1, q2, q3);
+          else rw[i][h] = enc4_exact<FMT>(q0, q1, q2, q3);
+        }
+      }
+    } else {
+      AbsMax<DT> am;
+      bool all_full = true;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + 4 * rg + i;
+        const char* src = xb + (r * p.ld_x + cc) * EB;
+        const bool full = r < p.rows && cc + 8 <= p.cols;  // vector loads, realigned if the row start is not
+        all_full &= full;
+        if (full) {
+          if constexpr (DT == kF32) {
+            uint4 ab[2];
+            load16_any<2>(src, ab);
+            const uint4 a = ab[0], b = ab[1];
+            am.add(a);
+            am.add(b);
+            f[i][0] = __uint_as_float(a.x); f[i][1] = __uint_as_float(a.y);
+            f[i][2] = __uint_as_float(a.z); f[i][3] = __uint_as_float(a.w);
+            f[i][4] = __uint_as_float(b.x); f[i][5] = __uint_as_float(b.y);
+            f[i][6] = __uint_as_float(b.z); f[i][7] = __uint_as_float(b.w);
+          } else {
+            uint4 a1[1];
+            load16_any<1>(src, a1);
+            const uint4 a = a1[0];
+            am.add(a);
+            widen2<DT>(a.x, f[i][0], f[i][1]); widen2<DT>(a.y, f[i][2], f[i][3]);
+            widen2<DT>(a.z, f[i][4], f[i][5]); widen2<DT>(a.w, f[i][6], f[i][7]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[i][e] = (r < p.rows && cc + e < p.cols) ? load1<DT>(p.x, r * p.ld_x + cc + e) : 0.0f;
+        }
+      }
+      bool nan;
+      float camax;
+      if (all_full) {  // every element came through a vector load
+        nan = am.has_nan();
+        camax = nan ? nan_free_absmax<32>(&f[0][0]) : am.value();
+      } else {
+        nan = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) nan |= f[i][e] != f[i][e];
+        camax = nan_free_absmax<32>(&f[0][0]);
+      }
+      amax = fmaxf(amax, camax);
+      if (!nan && sreg && camax * fabsf(s) <= FmtTraits<FMT>::kMax) {
+        // no clamp needed: fl32(|x| |s|) <= fl32(camax |s|) (monotonic rounding)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            rw[i][h] = cvt4_inrange<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
+                                         f[i][4 * h + 3] * s);
+      } else if (!nan && sreg) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            rw[i][h] = cvt4<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s, f[i][4 * h + 3] * s);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          f[i][e] = (r < p.rows && cc + e < p.cols) ? load1<DT>(p.x, r * p.ld_x + cc + e) : 0.0f;
-      }
-    }
-    bool nan;
-    float camax;
-    if (all_full) {  // every element came through a vector load
-      nan = am.has_nan();
-      camax = nan ? nan_free_absmax<32>(&f[0][0]) : am.value();
-    } else {
-      nan = false;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) nan |= f[i][e] != f[i][e];
-      camax = nan_free_absmax<32>(&f[0][0]);
-    }
-    amax = fmaxf(amax, camax);
-    uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
-    if (!nan && sreg && camax * fabsf(s) <= FmtTraits<FMT>::kMax) {
-      // no clamp needed: fl32(|x| |s|) <= fl32(camax |s|) (monotonic rounding)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          rw[i][h] = cvt4_inrange<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
+          for (int h = 0; h < 2; ++h)
+            rw[i][h] = enc4_exact<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
                                        f[i][4 * h + 3] * s);
-    } else if (!nan && sreg) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          rw[i][h] = cvt4<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s, f[i][4 * h + 3] * s);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          rw[i][h] = enc4_exact<FMT>(f[i][4 * h] * s, f[i][4 * h + 1] * s, f[i][4 * h + 2] * s,
-                                     f[i][4 * h + 3] * s);
+      }
     }
 
     if constexpr (MODE == kRow || MODE == kDual) {
