@@ -226,6 +226,29 @@ __device__ __forceinline__ void tile_coords(int64_t wg64, int64_t tiles_m64, int
   tn = (int64_t)(r / rows_here);
 }
 
+// Batched launches (grid x: the tiles of one batch, grid z: the batches):
+// workgroups are dealt to the XCDs round-robin in launch order, so a batch's
+// tiles would spread over several XCDs and each would fetch that batch's
+// operands into its own L2.  The launch-order index is remapped so that the
+// workgroups of one XCD take consecutive (batch, tile) pairs -- whole batches
+// where a batch's tiles divide the XCD's share.  Returns the tile index within
+// the batch in wg and the batch in bz.
+__device__ __forceinline__ void batch_tile(int64_t& wg, int64_t& bz) {
+  const uint64_t tiles = gridDim.x, total = tiles * gridDim.z;
+  const uint64_t lin = (uint64_t)blockIdx.z * tiles + blockIdx.x;
+  if (total <= 0xFFFFFFFFull) {  // 32-bit divisions (64-bit ones cost a few hundred instructions)
+    const uint32_t t32 = (uint32_t)tiles, l32 = (uint32_t)lin, full = (uint32_t)total / 8u * 8u;
+    const uint32_t id = l32 < full ? (l32 % 8u) * (full / 8u) + l32 / 8u : l32;
+    bz = id / t32;
+    wg = id % t32;
+  } else {
+    const uint64_t full = total / 8u * 8u;
+    const uint64_t id = lin < full ? (lin % 8u) * (full / 8u) + lin / 8u : lin;
+    bz = (int64_t)(id / tiles);
+    wg = (int64_t)(id % tiles);
+  }
+}
+
 // LAY: bit 0 -- A given K-major ([K, M], lda >= M), bit 1 -- B given K-major
 // ([K, N], ldb >= N); otherwise the operand is [rows, K] (NT).
 // Wait until at most r steps of LPW loads each are outstanding (r in [0, MAXR]).
@@ -258,10 +281,11 @@ template <int BM, int BN, int NWAVES, int DEEP> struct TileLds {
   static constexpr int kBytes = kRed + 4 * (NWAVES + 1);
 };
 
-// One BM x BN output tile at (m0, n0) of batch blockIdx.z, with `pool` the
+// One BM x BN output tile at (m0, n0) of batch bz, with `pool` the
 // workgroup's TileLds bytes.
 template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int OUT, int LAY, bool PREC, int DEEP>
-__device__ __forceinline__ void mm_tile(const MmArgs& p, const int64_t m0, const int64_t n0, uint8_t* pool) {
+__device__ __forceinline__ void mm_tile(const MmArgs& p, const int64_t m0, const int64_t n0, const int64_t bz,
+                                        uint8_t* pool) {
   constexpr bool KMA = (LAY & 1) != 0, KMB = (LAY & 2) != 0;
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -292,7 +316,6 @@ __device__ __forceinline__ void mm_tile(const MmArgs& p, const int64_t m0, const
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
-  const int64_t bz = blockIdx.z;
   const int ext_a = (int)(KMA ? p.a_extent_km(m0) : p.a_extent_from(m0));
   const int ext_b = (int)(KMB ? p.b_extent_km(n0) : p.b_extent_from(n0));
   const v4i rsa = buffer_rsrc(p.a + bz * p.stride_a + (KMA ? m0 : m0 * p.lda), ext_a);
@@ -721,9 +744,10 @@ template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOC
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) mm_fp8_dma(MmArgs p, int64_t tiles_m,
                                                                                  int64_t tiles_n, int group_m) {
   __shared__ __align__(16) uint8_t pool[TileLds<BM, BN, WAVES_M * WAVES_N, DEEP>::kBytes];
-  int64_t tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-  mm_tile<FA, FB, BM, BN, WAVES_M, WAVES_N, OUT, LAY, PREC, DEEP>(p, tm * BM, tn * BN, pool);
+  int64_t tm, tn, bz = 0, wg = blockIdx.x;
+  if (gridDim.z > 1) batch_tile(wg, bz);
+  tile_coords(wg, tiles_m, tiles_n, group_m, tm, tn);
+  mm_tile<FA, FB, BM, BN, WAVES_M, WAVES_N, OUT, LAY, PREC, DEEP>(p, tm * BM, tn * BN, bz, pool);
 }
 
 // Mixed grid for a last round of 256 x 256 tiles that would leave most CUs
@@ -743,11 +767,11 @@ __global__ void __launch_bounds__(512, 1) mm_fp8_mixed(MmArgs p, int64_t tiles_m
   int64_t tm, tn;
   if ((int64_t)blockIdx.x < nbig) {
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
-    mm_tile<FA, FB, 256, 256, 2, 4, OUT, LAY, false, 0>(p, tm * 256, tn * 256, pool);
+    mm_tile<FA, FB, 256, 256, 2, 4, OUT, LAY, false, 0>(p, tm * 256, tn * 256, 0, pool);
   } else {
     // nbig is a multiple of 8, so the band's own index keeps the XCD of blockIdx.x
     tile_coords((int64_t)blockIdx.x - nbig, band_tiles_m, band_tiles_n, group_m, tm, tn);
-    mm_tile<FA, FB, 128, 256, 2, 4, OUT, LAY, false, 0>(p, tm * 128, n_band + tn * 256, pool);
+    mm_tile<FA, FB, 128, 256, 2, 4, OUT, LAY, false, 0>(p, tm * 128, n_band + tn * 256, 0, pool);
   }
 }
 
