@@ -276,23 +276,37 @@ __device__ __forceinline__ void publish_max(uint32_t* p, float v) {
   wait_vmem();
 }
 
-// End of a ring-mode quantize workgroup; every thread of the block calls it
-// with the block's amax.  `flag` is one word of LDS.
+// First half of a workgroup's ring protocol, thread 0 only: max the block's
+// amax into its slot.  The atomic is left in flight (its old value returned
+// for ring_block_finish to consume), so a kernel that knows its amax before
+// storing its codes can publish it first and let the round trip overlap the
+// stores.
+__device__ __forceinline__ uint32_t ring_publish(uint32_t* ring, int H, float block_amax) {
+  const uint32_t nblk = gridDim.x * gridDim.y * gridDim.z;
+  const uint32_t nslot = nblk < (uint32_t)kFoldSlots ? nblk : (uint32_t)kFoldSlots;
+  const uint32_t bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  return dev_max(ring + H + 4 + (bid % nslot) * kFoldSlotStride, __float_as_uint(block_amax));
+}
+
+// Second half; every thread of the block calls it, thread 0 with the value
+// ring_publish returned.  Thread 0 waits for its published maximum (and
+// everything else its wave has in flight) to come back, takes the slot's
+// ticket, and the last member of a slot the completion ticket.  `flag` is
+// one word of LDS that no thread reads between the caller's last barrier and
+// this call.
 template <int FMT>
-__device__ void ring_block_done(uint32_t* ring, int H, float block_amax, float s_used, float* scale_inv_out,
-                                float* amax_out, uint32_t* flag) {
+__device__ void ring_block_finish(uint32_t* ring, int H, uint32_t published, float s_used, float* scale_inv_out,
+                                  float* amax_out, uint32_t* flag) {
   const uint32_t nblk = gridDim.x * gridDim.y * gridDim.z;
   const uint32_t nslot = nblk < (uint32_t)kFoldSlots ? nblk : (uint32_t)kFoldSlots;
   uint32_t* scratch = ring + H + 4;
   if (threadIdx.x == 0) {
+    asm volatile("" ::"v"(published));  // keep the returning form of the slot's atomic
+    wait_vmem();
     const uint32_t bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const uint32_t slot = bid % nslot;
-    uint32_t* sl = scratch + slot * kFoldSlotStride;
-    const uint32_t old = dev_max(sl, __float_as_uint(block_amax));
-    asm volatile("" ::"v"(old));  // keep the returning form of the atomic
-    wait_vmem();
     const uint32_t members = nblk / nslot + (slot < nblk % nslot ? 1u : 0u);
-    bool last = dev_add(sl + 1, 1u) == members - 1u;
+    bool last = dev_add(scratch + slot * kFoldSlotStride + 1, 1u) == members - 1u;
     if (last) last = dev_add(ring + H + 2, 1u) == nslot - 1u;
     *flag = last ? 1u : 0u;
   }
@@ -308,6 +322,15 @@ __device__ void ring_block_done(uint32_t* ring, int H, float block_amax, float s
     (void)dev_xchg(scratch + lane * kFoldSlotStride + 1, 0u);
   }
   if (lane == 0) (void)dev_xchg(ring + H + 2, 0u);
+}
+
+// End of a ring-mode quantize workgroup (both halves at once); every thread
+// of the block calls it with the block's amax.  `flag` is one word of LDS.
+template <int FMT>
+__device__ void ring_block_done(uint32_t* ring, int H, float block_amax, float s_used, float* scale_inv_out,
+                                float* amax_out, uint32_t* flag) {
+  const uint32_t published = threadIdx.x == 0 ? ring_publish(ring, H, block_amax) : 0u;
+  ring_block_finish<FMT>(ring, H, published, s_used, scale_inv_out, amax_out, flag);
 }
 
 }  // namespace fp8mi

@@ -204,11 +204,9 @@ constexpr int kFlatWaveStep = 64 * kFlatElemsPerThread;                   // 102
 constexpr int kFlatBlockStep = kFlatThreads * kFlatElemsPerThread;      // 4096 elements
 constexpr int kFlatUnroll = 2;                                          // block steps in flight per lane
 
-// Encode one lane's 16 elements of a wave step (already loaded) and store the codes.
-template <int DT, int FMT, int NL, int EPL>
-__device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t* out_w0, int lane, float s,
-                                                   bool sreg) {
-  float f[kFlatElemsPerThread];
+// One lane's 16 elements of a wave step as fp32 values.
+template <int DT, int NL>
+__device__ __forceinline__ void flat_widen(const uint4 (&v)[NL], float (&f)[kFlatElemsPerThread]) {
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -220,6 +218,26 @@ __device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t
       for (int e = 0; e < 4; ++e) widen2<DT>(w[e], f[j * 8 + 2 * e], f[j * 8 + 2 * e + 1]);
     }
   }
+}
+
+// Max |x| over one lane's 16 elements of a wave step, NaNs skipped -- the
+// value flat_encode_store returns for the same loads.
+template <int DT, int NL> __device__ __forceinline__ float flat_absmax(const uint4 (&v)[NL]) {
+  AbsMax<DT> am;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) am.add(v[j]);
+  if (!am.has_nan()) return am.value();
+  float f[kFlatElemsPerThread];
+  flat_widen<DT, NL>(v, f);
+  return nan_free_absmax<kFlatElemsPerThread>(f);
+}
+
+// Encode one lane's 16 elements of a wave step (already loaded) and store the codes.
+template <int DT, int FMT, int NL, int EPL>
+__device__ __forceinline__ float flat_encode_store(const uint4 (&v)[NL], uint8_t* out_w0, int lane, float s,
+                                                   bool sreg) {
+  float f[kFlatElemsPerThread];
+  flat_widen<DT, NL>(v, f);
   AbsMax<DT> am;
 #pragma unroll
   for (int j = 0; j < NL; ++j) am.add(v[j]);
@@ -292,6 +310,21 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
       amax = fmaxf(amax, flat_encode_store<DT, FMT, NL, EPL>(v[u], p.out_row + w0, lane, s, sreg));
     }
   };
+  if constexpr (!PF && !DYN) {
+    // A ring-mode workgroup whose whole share is one group knows its amax
+    // before it stores anything: it publishes first, so the slot atomic's
+    // round trip overlaps the encoding and the stores.
+    if (p.ring && ng == 1 && first + U == last) {
+      float a = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) a = fmaxf(a, flat_absmax<DT, NL>(va[u]));
+      const float bmax = block_max<kFlatThreads>(a, red);
+      const uint32_t pub = threadIdx.x == 0 ? ring_publish(p.ring, p.H, bmax) : 0u;
+      encode_group(va, first);
+      ring_block_finish<FMT>(p.ring, p.H, pub, s, p.scale_inv_out, p.amax_out, reinterpret_cast<uint32_t*>(red));
+      return;
+    }
+  }
   int64_t g = 0;
   if constexpr (PF) {
     uint4 vb[U][NL];
