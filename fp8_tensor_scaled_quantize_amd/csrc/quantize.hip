@@ -447,6 +447,11 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
   const int64_t t_first = (int64_t)bid * tiles_per_block;
   const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
   const bool x_rows16 = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 && ((p.ld_x * EB) & 15) == 0;
+  // A ring-mode workgroup of one transposed / dual tile publishes its amax as
+  // soon as the tile is encoded, before any of its codes are stored, so the
+  // slot atomic's round trip overlaps the stores.
+  const bool early = MODE != kRow && !DYN && p.ring != nullptr && t_last - t_first == 1;
+  uint32_t pub = 0u;
   for (int64_t tile = t_first; tile < t_last; ++tile) {
     int64_t r0, c0;
     tile_origin(tile, tiles_c, ntiles, r0, c0);
@@ -565,6 +570,10 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
       }
     }
 
+    if (early) {  // uniform over the workgroup
+      const float bm = block_max<kTileThreads>(amax, red);
+      if (t == 0) pub = ring_publish(p.ring, p.H, bm);
+    }
     if constexpr (MODE == kRow || MODE == kDual) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -639,6 +648,12 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
         }
       }
       __syncthreads();  // LDS reused by the next tile
+    }
+  }
+  if constexpr (MODE != kRow && !DYN) {
+    if (early) {
+      ring_block_finish<FMT>(p.ring, p.H, pub, s, p.scale_inv_out, p.amax_out, reinterpret_cast<uint32_t*>(red));
+      return;
     }
   }
   quant_block_done<FMT, kTileThreads, DYN>(p, amax, s, red);
