@@ -447,11 +447,14 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
   const int64_t t_first = (int64_t)bid * tiles_per_block;
   const int64_t t_last = t_first + tiles_per_block < ntiles ? t_first + tiles_per_block : ntiles;
   const bool x_rows16 = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0 && ((p.ld_x * EB) & 15) == 0;
-  // A ring-mode workgroup of one transposed / dual tile publishes its amax as
-  // soon as the tile is encoded, before any of its codes are stored, so the
-  // slot atomic's round trip overlaps the stores.
+  // A ring-mode workgroup of one transposed / dual tile publishes its amax
+  // before any of its codes are stored, so the slot atomic's round trip
+  // overlaps the stores: the general path as soon as its values are loaded
+  // (before encoding), the transposed fast path once the tile is encoded (a
+  // separate amax pass ahead of its row-by-row encode was slower).
   const bool early = MODE != kRow && !DYN && p.ring != nullptr && t_last - t_first == 1;
   uint32_t pub = 0u;
+  bool pubd = false;  // published already (the general path does it before encoding)
   for (int64_t tile = t_first; tile < t_last; ++tile) {
     int64_t r0, c0;
     tile_origin(tile, tiles_c, ntiles, r0, c0);
@@ -546,6 +549,11 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
         camax = nan_free_absmax<32>(&f[0][0]);
       }
       amax = fmaxf(amax, camax);
+      if (early) {  // uniform over the workgroup
+        const float bm = block_max<kTileThreads>(amax, red);
+        if (t == 0) pub = ring_publish(p.ring, p.H, bm);
+        pubd = true;
+      }
       if (!nan && sreg && camax * fabsf(s) <= FmtTraits<FMT>::kMax) {
         // no clamp needed: fl32(|x| |s|) <= fl32(camax |s|) (monotonic rounding)
 #pragma unroll
@@ -570,7 +578,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
       }
     }
 
-    if (early) {  // uniform over the workgroup
+    if (early && !pubd) {  // uniform over the workgroup
       const float bm = block_max<kTileThreads>(amax, red);
       if (t == 0) pub = ring_publish(p.ring, p.H, bm);
     }
