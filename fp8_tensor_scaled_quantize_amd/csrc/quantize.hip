@@ -380,6 +380,13 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
 constexpr int kTileR = 128, kTileC = 64, kTileThreads = 256;
 enum Mode : int { kRow = 0, kTrans = 1, kDual = 2 };
 
+// Bias-gradient partials in LDS: row group g (32 of them, 4 rows each) and
+// column c at g * 64 + (c ^ (g & 7)).  A write instruction (fixed column
+// offset e, lanes over 8 row groups x 8 column groups) then spreads over 32
+// distinct 8-byte bank pairs, and a read (one row group, 64 consecutive
+// columns) stays a permutation of one 512-byte row.
+__device__ __forceinline__ int bg_index(int g, int c) { return g * 64 + (c ^ (g & 7)); }
+
 __device__ __forceinline__ int lds_t_index(int c, int w) { return c * 32 + (w ^ (8 * ((c >> 3) & 3))); }
 
 // Tile origin (row, column) of a tile index: 32-bit division whenever the
@@ -436,7 +443,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
                                                                 int64_t tiles_per_block) {
   __shared__ float red[kTileThreads / 64];
   __shared__ __align__(16) uint32_t lds_t[(MODE == kRow) ? 1 : kTileC * 32];
-  __shared__ double bg_red[BG ? kTileThreads / 64 : 1][BG ? kTileC : 1];
+  __shared__ double bg_part[BG ? kTileR / 4 * kTileC : 1];  // [row group][column], swizzled
   constexpr int EB = In<DT>::kBytes;
   const float s = read_scale<FMT, DYN>(p);
   const bool sreg = scale_regular(s);
@@ -609,30 +616,22 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
       }
       if constexpr (BG) {
         // bias gradient: fp64 column sums of the raw values -- this thread's 4
-        // rows in order, the wave's 8 row groups by xor butterfly, then (after
-        // the barrier) the 4 waves in order
-        double cs[8];
+        // rows in order, parked in LDS by row group; after the barrier one
+        // thread per column adds the 32 row groups in order
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           double v = (double)f[0][e];
 #pragma unroll
           for (int i = 1; i < 4; ++i) v += (double)f[i][e];
-          v += __shfl_xor(v, 8, 64);
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
-          cs[e] = v;
-        }
-        if ((t & 63) < 8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bg_red[t >> 6][8 * cg + e] = cs[e];
+          bg_part[bg_index(rg, 8 * cg + e)] = v;
         }
       }
       __syncthreads();
       if constexpr (BG) {
         if (t < kTileC && c0 + t < p.cols) {
-          double v = bg_red[0][t];
+          double v = bg_part[bg_index(0, t)];
 #pragma unroll
-          for (int w = 1; w < kTileThreads / 64; ++w) v += bg_red[w][t];
+          for (int g = 1; g < kTileR / 4; ++g) v += bg_part[bg_index(g, t)];
           p.bias_ws[(r0 / kTileR) * p.cols + c0 + t] = v;
         }
       }
@@ -682,7 +681,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
                                                                 int64_t tiles_per_block) {
   __shared__ float red[kTileThreads / 64];
   __shared__ __align__(16) uint32_t lds_t[(MODE == kRow) ? 1 : kTileC * 32];
-  __shared__ double bg_red[BG ? kTileThreads / 64 : 1][BG ? kTileC : 1];
+  __shared__ double bg_part[BG ? kTileR / 4 * kTileC : 1];  // [row group][column], swizzled
   constexpr int EB = In<DT>::kBytes;
   constexpr int NLD = TileRaw<DT>::kLoads;
   const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
@@ -808,30 +807,22 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
       }
       if constexpr (BG) {
         // bias gradient: fp64 column sums of the raw values -- this thread's 4
-        // rows in order, the wave's 8 row groups by xor butterfly, then (after
-        // the barrier) the 4 waves in order
-        double cs[8];
+        // rows in order, parked in LDS by row group; after the barrier one
+        // thread per column adds the 32 row groups in order
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           double v = (double)f[0][e];
 #pragma unroll
           for (int i = 1; i < 4; ++i) v += (double)f[i][e];
-          v += __shfl_xor(v, 8, 64);
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
-          cs[e] = v;
-        }
-        if ((t & 63) < 8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bg_red[t >> 6][8 * cg + e] = cs[e];
+          bg_part[bg_index(rg, 8 * cg + e)] = v;
         }
       }
       __syncthreads();
       if constexpr (BG) {
         if (t < kTileC && c0 + t < p.cols) {
-          double v = bg_red[0][t];
+          double v = bg_part[bg_index(0, t)];
 #pragma unroll
-          for (int w = 1; w < kTileThreads / 64; ++w) v += bg_red[w][t];
+          for (int g = 1; g < kTileR / 4; ++g) v += bg_part[bg_index(g, t)];
           p.bias_ws[(r0 / kTileR) * p.cols + c0 + t] = v;
         }
       }
