@@ -24,6 +24,11 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # no hand-written or compiler-formed packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every atomic here is issued by one lane (or by lanes at distinct
+    # addresses): keep it a plain returning atomic whose value is waited for
+    # only where it is read (the optimizer's wave reduction reads it right
+    # after the issue)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"),
 ]
 

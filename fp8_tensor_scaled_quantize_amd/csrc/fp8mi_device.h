@@ -280,7 +280,9 @@ __device__ __forceinline__ void publish_max(uint32_t* p, float v) {
 // amax into its slot.  The atomic is left in flight (its old value returned
 // for ring_block_finish to consume), so a kernel that knows its amax before
 // storing its codes can publish it first and let the round trip overlap the
-// stores.
+// stores.  The library is built without the compiler's atomic optimizer,
+// which would turn this one-lane atomic into a wave reduction that needs the
+// returned value at once.
 __device__ __forceinline__ uint32_t ring_publish(uint32_t* ring, int H, float block_amax) {
   const uint32_t nblk = gridDim.x * gridDim.y * gridDim.z;
   const uint32_t nslot = nblk < (uint32_t)kFoldSlots ? nblk : (uint32_t)kFoldSlots;
@@ -289,9 +291,9 @@ __device__ __forceinline__ uint32_t ring_publish(uint32_t* ring, int H, float bl
 }
 
 // Second half; every thread of the block calls it, thread 0 with the value
-// ring_publish returned.  Thread 0 waits for its published maximum (and
-// everything else its wave has in flight) to come back, takes the slot's
-// ticket, and the last member of a slot the completion ticket.  `flag` is
+// ring_publish returned.  Thread 0 waits for its published maximum to come
+// back, takes the slot's ticket, and the last member of a slot the
+// completion ticket.  `flag` is
 // one word of LDS that no thread reads between the caller's last barrier and
 // this call.
 template <int FMT>
@@ -301,8 +303,11 @@ __device__ void ring_block_finish(uint32_t* ring, int H, uint32_t published, flo
   const uint32_t nslot = nblk < (uint32_t)kFoldSlots ? nblk : (uint32_t)kFoldSlots;
   uint32_t* scratch = ring + H + 4;
   if (threadIdx.x == 0) {
-    asm volatile("" ::"v"(published));  // keep the returning form of the slot's atomic
-    wait_vmem();
+    // the slot's atomic must have come back: the compiler waits for its value
+    // here (a wave's vector memory operations complete in issue order, so
+    // stores issued after the atomic may stay in flight -- the fold reads
+    // none of them)
+    asm volatile("" ::"v"(published) : "memory");
     const uint32_t bid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const uint32_t slot = bid % nslot;
     const uint32_t members = nblk / nslot + (slot < nblk % nslot ? 1u : 0u);

@@ -319,7 +319,8 @@ __global__ void __launch_bounds__(kFlatThreads) quantize_flat(QuantArgs p, int64
 #pragma unroll
       for (int u = 0; u < U; ++u) a = fmaxf(a, flat_absmax<DT, NL>(va[u]));
       const float bmax = block_max<kFlatThreads>(a, red);
-      const uint32_t pub = threadIdx.x == 0 ? ring_publish(p.ring, p.H, bmax) : 0u;
+      uint32_t pub = __builtin_nondeterministic_value(0u);  // read by thread 0 only
+      if (threadIdx.x == 0) pub = ring_publish(p.ring, p.H, bmax);
       encode_group(va, first);
       ring_block_finish<FMT>(p.ring, p.H, pub, s, p.scale_inv_out, p.amax_out, reinterpret_cast<uint32_t*>(red));
       return;
@@ -460,7 +461,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
   // (before encoding), the transposed fast path once the tile is encoded (a
   // separate amax pass ahead of its row-by-row encode was slower).
   const bool early = MODE != kRow && !DYN && p.ring != nullptr && t_last - t_first == 1;
-  uint32_t pub = 0u;
+  uint32_t pub = __builtin_nondeterministic_value(0u);  // read by thread 0 only
   bool pubd = false;  // published already (the general path does it before encoding)
   for (int64_t tile = t_first; tile < t_last; ++tile) {
     int64_t r0, c0;
