@@ -439,7 +439,11 @@ __device__ __forceinline__ void transpose4x4_bytes(uint32_t a, uint32_t b, uint3
 
 // One-shot form: each workgroup loads, encodes and stores its tiles in turn
 // (launched with one tile per workgroup; low registers, high occupancy).
-template <int DT, int FMT, int MODE, bool BG, bool DYN>
+// AL: every tile lies inside the tensor and every row of x, the row codes
+// and the transposed codes starts 16 / 8 / 16 bytes aligned (checked by the
+// launcher), so no bounds or alignment tests and no element-wise fallbacks
+// are compiled -- which also lets the compiler count the stores exactly.
+template <int DT, int FMT, int MODE, bool BG, bool DYN, bool AL>
 __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int64_t tiles_c, int64_t ntiles,
                                                                 int64_t tiles_per_block) {
   __shared__ float red[kTileThreads / 64];
@@ -469,7 +473,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
     const int64_t cc = c0 + 8 * cg;  // this thread's first column
     uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
     float f[4][8];      // the values (general path; the bias gradient reads them)
-    if (MODE == kTrans && x_rows16 && r0 + kTileR <= p.rows && c0 + kTileC <= p.cols) {
+    if (MODE == kTrans && (AL || (x_rows16 && r0 + kTileR <= p.rows && c0 + kTileC <= p.cols))) {
       // transposed output, tile inside the tensor, rows on 16 bytes: the four
       // rows' loads go out back to back, then each row is encoded on its own
       // (its own NaN and in-range tests, which give the same codes as the
@@ -516,7 +520,7 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
       for (int i = 0; i < 4; ++i) {
         const int64_t r = r0 + 4 * rg + i;
         const char* src = xb + (r * p.ld_x + cc) * EB;
-        const bool full = r < p.rows && cc + 8 <= p.cols;  // vector loads, realigned if the row start is not
+        const bool full = AL || (r < p.rows && cc + 8 <= p.cols);  // vector loads, realigned if the row start is not
         all_full &= full;
         if (full) {
           if constexpr (DT == kF32) {
@@ -594,9 +598,9 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t r = r0 + 4 * rg + i;
-        if (r >= p.rows) continue;
+        if (!AL && r >= p.rows) continue;
         uint8_t* dst = p.out_row + r * p.ld_row + cc;
-        if (cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
+        if (AL || (cc + 8 <= p.cols && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0))) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(rw[i][0], rw[i][1]);
         } else {
 #pragma unroll
@@ -642,10 +646,10 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled(QuantArgs p, int6
         const int cl = (t >> 3) + 32 * pass, q = t & 7;
         const int64_t c = c0 + cl;
         const int64_t rr = r0 + 16 * q;
-        if (c < p.cols && rr < p.rows) {
+        if (AL || (c < p.cols && rr < p.rows)) {
           const uint4 v = *reinterpret_cast<const uint4*>(&lds_t[lds_t_index(cl, 4 * q)]);
           uint8_t* dst = p.out_t + c * p.ld_t + rr;
-          if (rr + 16 <= p.rows && ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0)) {
+          if (AL || (rr + 16 <= p.rows && ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0))) {
             *reinterpret_cast<uint4*>(dst) = v;
           } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -1011,11 +1015,31 @@ constexpr int kPersistBlocksPerCU = 3;
 // they were as slow (transposed 19.4 us) or slower (dual 23.2 against 21.8).
 constexpr int kAmaxOutBlocksPerCU = 1;
 
+// Whole aligned tiles for the one-shot transposed / dual kernel (its AL form).
+template <int DT> static bool tiles_aligned(const QuantArgs& p, int mode) {
+  constexpr int EB = In<DT>::kBytes;
+  const auto a = [](const void* q, unsigned m) { return (reinterpret_cast<uintptr_t>(q) & m) == 0; };
+  if (p.rows % kTileR != 0 || p.cols % kTileC != 0) return false;
+  if (!a(p.x, 15u) || ((p.ld_x * EB) & 15) != 0) return false;
+  if (mode == kDual && (!a(p.out_row, 7u) || (p.ld_row & 7) != 0)) return false;
+  return a(p.out_t, 15u) && (p.ld_t & 15) == 0;
+}
+
 template <int DT, int FMT, int M, bool BG, bool DYN>
 static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantArgs& p, int64_t tiles_c,
                          int64_t ntiles, int64_t tpb) {
   if (one_shot) {
-    hipLaunchKernelGGL((quantize_tiled<DT, FMT, M, BG, DYN>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles, tpb);
+    // The AL form measured faster for transposed grids of every size and for
+    // dual grids of up to 3 workgroups per CU (bf16 x 1536 columns, graph
+    // replay: 4096 rows 10.2 -> 8.9 us), slower for denser dual grids (6144
+    // rows 11.5 -> 11.9, 8192 rows 13.4 -> 14.6 us).
+    const bool al_grid = M == kTrans || ntiles <= 3 * (int64_t)device_cu_count();
+    if (M != kRow && al_grid && tiles_aligned<DT>(p, M))
+      hipLaunchKernelGGL((quantize_tiled<DT, FMT, M, BG, DYN, true>), grid, dim3(kTileThreads), 0, st, p, tiles_c,
+                         ntiles, tpb);
+    else
+      hipLaunchKernelGGL((quantize_tiled<DT, FMT, M, BG, DYN, false>), grid, dim3(kTileThreads), 0, st, p, tiles_c,
+                         ntiles, tpb);
   } else {
     hipLaunchKernelGGL((quantize_tiled_pf<DT, FMT, M, BG, DYN>), grid, dim3(kTileThreads), 0, st, p, tiles_c, ntiles,
                        tpb);

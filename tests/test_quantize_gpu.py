@@ -145,6 +145,37 @@ def test_ring_fold_sequence(layout, fmt, fid):
         ring_o = ref["ring"]
 
 
+
+@pytest.mark.parametrize("dtype", O.DTYPES)
+@pytest.mark.parametrize("shape", [(256, 256), (512, 128), (2048, 1536)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_ring_sequence_whole_aligned_tiles(shape, dtype):
+    """Ring mode on tensors of whole 128 x 64 tiles with aligned rows (the
+    one-shot kernels' specialised form and their early amax publication):
+    codes, scale_inv, amax and ring words bit-exact over 6 calls per layout."""
+    fmt, fid = FMTS[0]
+    for layout in ("row", "t", "dual"):
+        ring_o = O.Ring.new(4, 3.0)
+        ring = ring_from_oracle(ring_o)
+        for step in range(6):
+            x = synth.gaussian(shape, [1.0, 20.0, 0.05][step % 3], dtype, 5, step, O.DTYPES.index(dtype))
+            ref = O.quantize(x, dtype, fmt, ring=ring_o)
+            xd = to_device(x, dtype)
+            si, am = scalar(0), scalar(0)
+            if layout == "dual":
+                r, t = fp8mi.fp8_quantize_dual(xd, fid, ring=ring, scale_inv_out=si, amax_out=am)
+                got, want = [np_codes(r), np_codes(t)], [ref["codes"], ref["codes_t"]]
+            else:
+                o = fp8mi.fp8_quantize(xd, fid, layout == "t", ring=ring, scale_inv_out=si, amax_out=am)
+                got, want = [np_codes(o)], [ref["codes_t"] if layout == "t" else ref["codes"]]
+            torch.cuda.synchronize()
+            tag = f"{layout} step {step}"
+            for g, w in zip(got, want):
+                assert np.array_equal(g, w), tag
+            assert f32_bits(si) == as_bits(ref["scale_inv"]), tag
+            assert f32_bits(am) == as_bits(ref["amax"]), tag
+            assert np.array_equal(ring_state_words(ring), ref["ring"].words()), tag
+            ring_o = ref["ring"]
+
 @pytest.mark.parametrize("fmt,fid", FMTS)
 def test_in_kernel_fold_equals_standalone_fold(fmt, fid):
     """The quantize kernel's last-block fold and fp8_amax_fold of the same
