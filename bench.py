@@ -194,10 +194,10 @@ TRAFFIC_KERNELS = {
     ("mm_fp8_dma<0, 0, 256, 256, 2, 4, 1, 0, 0, false, 0>", 131072): "mm_fp8_out_e4m3",
     ("mm_fp8_dma<0, 0, 256, 256, 2, 4, 1, -1, 3, false, 0>", 131072): "mm_fp8_kmajor",
     ("quantize_flat<2, 0, false, false>", 393216): "quantize_row",
-    ("quantize_tiled<2, 0, 1, false, false>", 393216): "quantize_transposed",
-    ("quantize_tiled<2, 0, 2, false, false>", 393216): "quantize_dual",
+    ("quantize_tiled<2, 0, 1, false, false, true>", 393216): "quantize_transposed",
+    ("quantize_tiled<2, 0, 2, false, false, false>", 393216): "quantize_dual",
     ("quantize_flat<2, 0, false, true>", 393216): "quantize_dynamic_row_pass",
-    ("quantize_tiled<2, 0, 2, false, true>", 393216): "quantize_dynamic_dual_pass",
+    ("quantize_tiled<2, 0, 2, false, true, false>", 393216): "quantize_dynamic_dual_pass",
     ("amax_partials<2>", 196864): "amax_pass_8192x1536",
     ("stream_kernel<true>", 393216): "stream_reference_row_bytes",
     ("stream_kernel<false>", 393216): "stream_reference_dual_bytes",
