@@ -217,6 +217,52 @@ def test_empty_and_degenerate_shapes():
     assert o.shape == (0, 5)
 
 
+# bf16 inputs are stored as uint16 bit patterns: plant specials by their bits
+_SPECIAL_BF16 = {"nan": 0x7FC0, "-nan": 0xFFC0, "inf": 0x7F80, "-inf": 0xFF80}
+_SPECIAL_FLOAT = {"nan": np.nan, "-nan": -np.nan, "inf": np.inf, "-inf": -np.inf}
+
+
+def special(x, dtype, i, j, kind):
+    x[i, j] = _SPECIAL_BF16[kind] if dtype == "bf16" else _SPECIAL_FLOAT[kind]
+
+
+@pytest.mark.parametrize("dtype", O.DTYPES)
+@pytest.mark.parametrize("shape", [(512, 1024), (256, 256), (300, 200)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_ring_sequence_with_nan_and_inf(shape, dtype):
+    """Ring mode with NaN and infinities planted in different workgroups'
+    shares (the one-shot row kernel, the aligned and general tiled forms,
+    each publishing its amax before storing): NaN never reaches amax, an
+    infinite amax folds into the window, codes and ring words bit-exact."""
+    fmt, fid = FMTS[1]
+    rows, cols = shape
+    for layout in ("row", "t", "dual"):
+        ring_o = O.Ring.new(3, 2.0)
+        ring = ring_from_oracle(ring_o)
+        for step in range(4):
+            x = synth.gaussian(shape, 1.0, dtype, 8, step, O.DTYPES.index(dtype))
+            special(x, dtype, (7 * step + 1) % rows, (13 * step + 5) % cols, "nan")
+            special(x, dtype, rows - 1 - step, step, "-nan")
+            if step in (1, 2):
+                special(x, dtype, rows // 2, cols // 3 + step, "inf" if step == 1 else "-inf")
+            ref = O.quantize(x, dtype, fmt, ring=ring_o)
+            xd = to_device(x, dtype)
+            si, am = scalar(0), scalar(0)
+            if layout == "dual":
+                r, t = fp8mi.fp8_quantize_dual(xd, fid, ring=ring, scale_inv_out=si, amax_out=am)
+                got, want = [np_codes(r), np_codes(t)], [ref["codes"], ref["codes_t"]]
+            else:
+                o = fp8mi.fp8_quantize(xd, fid, layout == "t", ring=ring, scale_inv_out=si, amax_out=am)
+                got, want = [np_codes(o)], [ref["codes_t"] if layout == "t" else ref["codes"]]
+            torch.cuda.synchronize()
+            tag = f"{layout} step {step}"
+            for g, w in zip(got, want):
+                assert np.array_equal(g, w), tag
+            assert f32_bits(si) == as_bits(ref["scale_inv"]), tag
+            assert f32_bits(am) == as_bits(ref["amax"]), tag
+            assert np.array_equal(ring_state_words(ring), ref["ring"].words()), tag
+            ring_o = ref["ring"]
+
+
 def test_amax_ignores_scale_and_nan():
     """amax comes from the raw values: a huge scale that saturates every code
     leaves amax unchanged; NaN inputs do not reach it."""
