@@ -367,10 +367,13 @@ def code_tokens(src: str) -> str:
 
 def kernel_source_hash():
     """sha256 of the code (comments and layout ignored) of the HIP sources
-    that hold or feed the kernels: counters taken on other code are stale."""
+    that hold or feed the kernels, and of the compiler flags they are built
+    with: counters taken on other code are stale."""
     import hashlib
+    from fp8_tensor_scaled_quantize_amd import build as _build
     csrc = os.path.join(ROOT, "fp8_tensor_scaled_quantize_amd", "csrc")
     h = hashlib.sha256()
+    h.update(repr((_build.HIPCC_FLAGS[:-2], sorted(_build.EXTRA_FLAGS.items()))).encode())  # include path dropped
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h")) and name not in HOST_ONLY_SOURCES:
             h.update(name.encode())
