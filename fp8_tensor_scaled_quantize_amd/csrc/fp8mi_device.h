@@ -235,7 +235,8 @@ __device__ void ring_fold_wave(uint32_t* ring, int H, float v, float* scale_inv_
 // takes the last completion ticket reduces the slots, folds, and clears the
 // scratch.  Ordering rests on returning device-scope atomics: every atomic
 // below returns its old value, and a workgroup waits for each to come back
-// (s_waitcnt vmcnt(0)) before issuing the next, so its partial amax is
+// (s_waitcnt on the vector memory counter, which the wave's operations
+// decrement in issue order) before issuing the next, so its partial amax is
 // performed at the device's coherence point before its ticket is; the slot
 // and completion tickets are totally ordered per address, and the final
 // reads are device-scope atomic loads.  No L2 write-back fence is needed
@@ -293,9 +294,8 @@ __device__ __forceinline__ uint32_t ring_publish(uint32_t* ring, int H, float bl
 // Second half; every thread of the block calls it, thread 0 with the value
 // ring_publish returned.  Thread 0 waits for its published maximum to come
 // back, takes the slot's ticket, and the last member of a slot the
-// completion ticket.  `flag` is
-// one word of LDS that no thread reads between the caller's last barrier and
-// this call.
+// completion ticket.  `flag` is one word of LDS that no thread reads between
+// the caller's last barrier and this call.
 template <int FMT>
 __device__ void ring_block_finish(uint32_t* ring, int H, uint32_t published, float s_used, float* scale_inv_out,
                                   float* amax_out, uint32_t* flag) {
