@@ -616,6 +616,16 @@ __device__ __forceinline__ void mm_tile(const MmArgs& p, const int64_t m0, const
     constexpr int CROW8 = BN + 16;
     uint8_t* Cs = smem;
     const bool fast = !__any(amax != amax) && sreg;
+    // the amax leaves NaN out (fmaxf returns the other operand for a NaN)
+    if (!fast) amax = tile_max([](float a, float b) { return fmaxf(a, b); });
+    // With an output ring the workgroup's amax is published before any code is
+    // encoded or stored (its atomic's round trip overlaps them); the tickets
+    // follow the stores.
+    uint32_t pub = __builtin_nondeterministic_value(0u);  // read by thread 0 only
+    if (p.c_ring) {
+      const float bmax = block_max<64 * NWAVES>(amax, red_c);
+      if (threadIdx.x == 0) pub = ring_publish(p.c_ring, p.c_H, bmax);
+    }
     // With no lane's fl32(amax |s|) above fmt_max no code needs the clamp:
     // fl32(|y| |s|) <= fl32(amax |s|) since rounding is monotonic.
     if (fast && !__any(amax * fabsf(s_c) > FmtTraits<OUT>::kMax)) {
@@ -637,8 +647,6 @@ __device__ __forceinline__ void mm_tile(const MmArgs& p, const int64_t m0, const
               cvt4<OUT>(y[0] * s_c, y[1] * s_c, y[2] * s_c, y[3] * s_c);
         }
     } else {
-      // the amax leaves NaN out (fmaxf returns the other operand for a NaN)
-      amax = tile_max([](float a, float b) { return fmaxf(a, b); });
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -671,16 +679,18 @@ __device__ __forceinline__ void mm_tile(const MmArgs& p, const int64_t m0, const
         }
       }
     }
-    // amax of this workgroup's outputs, then the cross-workgroup publication:
-    // the ring protocol (the last workgroup folds), or an atomic max into the
+    // the cross-workgroup publication: the ring protocol's tickets (the last
+    // workgroup folds), or an atomic max of this workgroup's amax into the
     // caller's word (zeroed before the launch)
-    const float bmax = block_max<64 * NWAVES>(amax, red_c);
     if (p.c_ring) {
-      ring_block_done<OUT>(p.c_ring, p.c_H, bmax, s_c, p.c_scale_inv_out, p.c_amax_out,
-                           reinterpret_cast<uint32_t*>(red_c + NWAVES));
-    } else if (threadIdx.x == 0) {
-      if (p.c_amax_out) publish_max(reinterpret_cast<uint32_t*>(p.c_amax_out), bmax);
-      if (p.c_scale_inv_out && blockIdx.x == 0 && blockIdx.z == 0) *p.c_scale_inv_out = 1.0f / s_c;
+      ring_block_finish<OUT>(p.c_ring, p.c_H, pub, s_c, p.c_scale_inv_out, p.c_amax_out,
+                             reinterpret_cast<uint32_t*>(red_c + NWAVES));
+    } else {
+      const float bmax = block_max<64 * NWAVES>(amax, red_c);
+      if (threadIdx.x == 0) {
+        if (p.c_amax_out) publish_max(reinterpret_cast<uint32_t*>(p.c_amax_out), bmax);
+        if (p.c_scale_inv_out && blockIdx.x == 0 && blockIdx.z == 0) *p.c_scale_inv_out = 1.0f / s_c;
+      }
     }
     return;
   }
