@@ -263,6 +263,35 @@ def test_ring_sequence_with_nan_and_inf(shape, dtype):
             ring_o = ref["ring"]
 
 
+@pytest.mark.parametrize("out_case", ["row_misaligned", "t_padded", "t_misaligned"])
+def test_whole_tiles_with_unaligned_outputs(out_case):
+    """Whole 128 x 64 tiles and an aligned input, but an output whose base or
+    row pitch is not aligned: the one-shot kernel must take its general form
+    (the aligned form stores 8 / 16 bytes at a time) and still give the
+    oracle's bytes with the padding untouched, explicit scale and ring."""
+    rows, cols = 256, 128
+    x = synth.gaussian((rows, cols), 1.0, "bf16", 10, ["row_misaligned", "t_padded", "t_misaligned"].index(out_case))
+    xd = to_device(x, "bf16")
+    fmt, fid = FMTS[0]
+    o_row = codes_out(rows, cols, cols, 3 if out_case == "row_misaligned" else 0)
+    o_t = codes_out(cols, rows, rows + (8 if out_case == "t_padded" else 0), 5 if out_case == "t_misaligned" else 0)
+    ring_o = O.Ring.new(4, 7.0)
+    ring = ring_from_oracle(ring_o)
+    ref = O.quantize(x, "bf16", fmt, ring=ring_o)
+    fp8mi.fp8_quantize_dual(xd, fid, out_row=o_row, out_t=o_t, ring=ring)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_codes(o_row), ref["codes"])
+    assert np.array_equal(np_codes(o_t), ref["codes_t"])
+    assert padding_untouched(o_row) and padding_untouched(o_t)
+    assert np.array_equal(ring_state_words(ring), ref["ring"].words())
+    o_t2 = codes_out(cols, rows, rows + (8 if out_case == "t_padded" else 0), 5 if out_case == "t_misaligned" else 0)
+    s = np.float32(3.5)
+    fp8mi.fp8_quantize(xd, fid, True, out=o_t2, scale=scalar(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(np_codes(o_t2), O.quantize(x, "bf16", fmt, scale=s)["codes_t"])
+    assert padding_untouched(o_t2)
+
+
 def test_amax_ignores_scale_and_nan():
     """amax comes from the raw values: a huge scale that saturates every code
     leaves amax unchanged; NaN inputs do not reach it."""
