@@ -716,6 +716,9 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
     }
   };
 
+  // In ring mode a workgroup publishes its amax at its last tile, once that
+  // tile's values are in and before its codes are stored (see quantize_tiled).
+  uint32_t pub = __builtin_nondeterministic_value(0u);  // read by thread 0 only
   auto process_tile = [&](int64_t tile, const TileRaw<DT>& L, float s, bool sreg) {
     int64_t r0, c0;
     tile_origin(tile, tiles_c, ntiles, r0, c0);
@@ -761,6 +764,12 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
       camax = nan_free_absmax<32>(&f[0][0]);
     }
     amax = fmaxf(amax, camax);
+    if constexpr (!DYN) {
+      if (p.ring != nullptr && tile + t_step >= ntiles) {  // uniform over the workgroup
+        const float bm = block_max<kTileThreads>(amax, red);
+        if (t == 0) pub = ring_publish(p.ring, p.H, bm);
+      }
+    }
     uint32_t rw[4][2];  // row words: rw[i][h] = codes of row i, columns 4h..4h+3
     if (!nan && sreg && camax * fabsf(s) <= FmtTraits<FMT>::kMax) {
       // no clamp needed: fl32(|x| |s|) <= fl32(camax |s|) (monotonic rounding)
@@ -865,6 +874,12 @@ __global__ void __launch_bounds__(kTileThreads) quantize_tiled_pf(QuantArgs p, i
     if (tile + t_step < ntiles) load_tile(tile + t_step, nxt);
     process_tile(tile, cur, s, sreg);
     cur = nxt;
+  }
+  if constexpr (!DYN) {
+    if (p.ring != nullptr && t_first < ntiles) {
+      ring_block_finish<FMT>(p.ring, p.H, pub, s, p.scale_inv_out, p.amax_out, reinterpret_cast<uint32_t*>(red));
+      return;
+    }
   }
   quant_block_done<FMT, kTileThreads, DYN>(p, amax, s, red);
 }
