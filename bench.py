@@ -197,7 +197,7 @@ TRAFFIC_KERNELS = {
     ("quantize_tiled<2, 0, 1, false, false, true>", 393216): "quantize_transposed",
     ("quantize_tiled<2, 0, 2, false, false, false>", 393216): "quantize_dual",
     ("quantize_flat<2, 0, false, true>", 393216): "quantize_dynamic_row_pass",
-    ("quantize_tiled<2, 0, 2, false, true, false>", 393216): "quantize_dynamic_dual_pass",
+    ("quantize_tiled<2, 0, 2, false, true, true>", 393216): "quantize_dynamic_dual_pass",
     ("amax_partials<2>", 196864): "amax_pass_8192x1536",
     ("stream_kernel<true>", 393216): "stream_reference_row_bytes",
     ("stream_kernel<false>", 393216): "stream_reference_dual_bytes",

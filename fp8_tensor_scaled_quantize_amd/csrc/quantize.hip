@@ -1044,11 +1044,13 @@ template <int DT, int FMT, int M, bool BG, bool DYN>
 static void launch_tiled(bool one_shot, dim3 grid, hipStream_t st, const QuantArgs& p, int64_t tiles_c,
                          int64_t ntiles, int64_t tpb) {
   if (one_shot) {
-    // The AL form measured faster for transposed grids of every size and for
+    // The AL form measured faster for transposed grids of every size, for
     // dual grids of up to 3 workgroups per CU (bf16 x 1536 columns, graph
-    // replay: 4096 rows 10.2 -> 8.9 us), slower for denser dual grids (6144
-    // rows 11.5 -> 11.9, 8192 rows 13.4 -> 14.6 us).
-    const bool al_grid = M == kTrans || ntiles <= 3 * (int64_t)device_cu_count();
+    // replay: 4096 rows 10.2 -> 8.9 us) and for current-scaling dual passes
+    // (8192 rows: the call 17.5 -> 16.9 us); slower for denser dual grids
+    // with a ring or an explicit scale (6144 rows 11.5 -> 11.9, 8192 rows
+    // 13.4 -> 14.6 us).
+    const bool al_grid = M == kTrans || DYN || ntiles <= 3 * (int64_t)device_cu_count();
     if (M != kRow && al_grid && tiles_aligned<DT>(p, M))
       hipLaunchKernelGGL((quantize_tiled<DT, FMT, M, BG, DYN, true>), grid, dim3(kTileThreads), 0, st, p, tiles_c,
                          ntiles, tpb);
